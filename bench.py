@@ -1,0 +1,276 @@
+"""Benchmark of the weight-only MXFP4 / INT4 decode projections on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Default workload (the headline): the SmolLM3-3B-shaped decode MLP gate/up,
+hidden 2048, intermediate 11008, batch 1, MXFP4 gate and up with row
+postscales, fused SwiGLU.  One step is one token through all 24 layers' gate/up
+projections (24 calls, each on a different layer's weights, so the 577 MB
+working set defeats the 256 MB Infinity Cache).  Inputs are synthetic (seeded,
+workloads.py) and resident in HBM before timing starts.
+
+Prints one JSON line: value = effective HBM GB/s over the algorithmic bytes
+(each packed weight byte, E8M0 scale, postscale, activation and output once),
+with us_per_call, the roofline of the kernel and the CPU oracle timed on the
+host (a reported baseline, not a target).
+
+Other workloads (--workload): tiny, phi4 (gate/up), phi4-int4 (QKV + O),
+gptoss (route + expert gate/up + down), batched (--batch B).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def gateup_bytes(inter, hidden, batch, out_bytes=4):
+    codes = 2 * inter * hidden // 2
+    scales = 2 * inter * hidden // 32
+    ps = 2 * inter * 4
+    return codes + scales + ps + batch * hidden * 2 + batch * inter * out_bytes
+
+
+def mx_matrix_bytes(n, k):
+    return n * k // 2 + n * k // 32 + n * 4
+
+
+def int4_bytes(n, k, batch):
+    return n * k // 2 + n * (-(-k // 128)) * 4 + batch * k * 2 + batch * n * 4
+
+
+def setup_gateup(tt, torch, dev, w, layers, batch, distinct=None):
+    """Packed gate/up weights of `layers` layers on the device; the first
+    `distinct` are generated, the rest are device copies of them."""
+    import workloads
+    distinct = layers if distinct is None else distinct
+    packs = []
+    for layer in range(distinct):
+        g, u = workloads.gateup(w, layer)
+        packs.append(torch.from_numpy(tt.pack_mxfp4_gateup(g, u, w.inter, w.hidden)).to(dev))
+    while len(packs) < layers:
+        packs.append(packs[len(packs) % distinct].clone())
+    xs = [torch.from_numpy(workloads.activations(w.wid, layer, batch, w.hidden).view(np.int16))
+          .to(dev) for layer in range(layers)]
+    return packs, xs
+
+
+def time_steps(torch, step, steps, warmup):
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / 1e3  # seconds
+
+
+def cpu_baseline_gateup(w, seconds):
+    """The oracle, untuned, single-threaded, on full layers of the same
+    workload until about `seconds` of CPU work."""
+    import oracle
+    import workloads
+    t_total, calls, nbytes = 0.0, 0, 0
+    layer = 0
+    while t_total < seconds and layer < w.layers:
+        g, u = workloads.gateup(w, layer)
+        x = workloads.activations(w.wid, layer, 1, w.hidden)
+        t0 = time.perf_counter()
+        oracle.mxfp4_gateup_swiglu(g, u, w.inter, w.hidden, x)
+        t_total += time.perf_counter() - t0
+        calls += 1
+        nbytes += gateup_bytes(w.inter, w.hidden, 1)
+        layer += 1
+    return dict(value=round(nbytes / t_total / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                us_per_call=round(t_total / calls * 1e6, 1),
+                sample=f"{calls} full {w.name} layer calls (batch 1), single thread, "
+                       f"fp64 oracle, {t_total:.1f} s")
+
+
+def run(args):
+    import torch
+
+    import bit_weight_only_mxfp4_amd as tt
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    K, W = args.steps, args.warmup
+    result = None
+
+    if args.workload in ("smollm3", "tiny", "phi4", "batched"):
+        w = {"smollm3": workloads.SMOLLM3, "tiny": workloads.TINY, "phi4": workloads.PHI4,
+             "batched": workloads.BATCHED}[args.workload]
+        batch = args.batch if args.workload == "batched" else 1
+        layers = w.layers
+        distinct = min(layers, 4) if args.workload == "phi4" else layers
+        log(f"setup {w.name}: {layers} layers, batch {batch}")
+        packs, xs = setup_gateup(tt, torch, dev, w, layers, batch, distinct)
+        outs = [torch.empty((batch, w.inter), dtype=torch.float32, device=dev)
+                for _ in range(layers)]
+
+        def step():
+            for i in range(layers):
+                tt.mxfp4_gateup_swiglu(packs[i], w.inter, w.hidden, xs[i], out=outs[i])
+
+        secs = time_steps(torch, step, K, W)
+        calls = K * layers
+        per_call = gateup_bytes(w.inter, w.hidden, batch)
+        us_call = secs / calls * 1e6
+        gbs = per_call * calls / secs / 1e9
+        kernel = "k_gateup_valu" if batch == 1 else "k_gateup_mfma"
+        result = dict(metric="effective HBM GB/s of the MXFP4 gate/up SwiGLU GEMV "
+                             "(us/call alongside)",
+                      value=round(gbs, 2), unit="GB/s", us_per_call=round(us_call, 3),
+                      ms_per_step=round(secs / K * 1e3, 4), bytes_per_call=per_call,
+                      config=dict(workload=w.name, hidden=w.hidden, inter=w.inter, batch=batch,
+                                  layers_rotated=layers, calls_per_step=layers),
+                      roofline=dict(bound="hbm", kernel=kernel, achieved=round(gbs, 2),
+                                    peak=PEAK_HBM_GBS, unit="GB/s",
+                                    frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
+        if not args.no_cpu_baseline and args.workload in ("smollm3", "tiny"):
+            log("cpu baseline (oracle) ...")
+            result["cpu_baseline"] = cpu_baseline_gateup(w, args.cpu_seconds)
+
+    elif args.workload == "phi4-int4":
+        w = workloads.PHI4
+        (nq, kq), (no, ko) = workloads.attention_shapes(w)
+        copies, distinct = 16, 2
+        log(f"setup INT4 QKV [{nq}x{kq}] and O [{no}x{ko}], {copies} copies")
+        packs = []
+        for layer in range(distinct):
+            pr = []
+            for (n, k, tid) in ((nq, kq, workloads.T_INT4W), (no, ko, workloads.T_INT4W + 100)):
+                q, s, z = tt.quantize_int4_affine(workloads.int4_source(w.wid, layer, n, k, tid))
+                pr.append(torch.from_numpy(tt.pack_int4(q, s, z, n, k)).to(dev))
+            packs.append(pr)
+        while len(packs) < copies:
+            packs.append([p.clone() for p in packs[len(packs) % distinct]])
+        x = torch.from_numpy(workloads.activations(w.wid, 0, 1, kq, workloads.T_OX)
+                             .view(np.int16)).to(dev)
+        yq = torch.empty((1, nq), dtype=torch.float32, device=dev)
+        yo = torch.empty((1, no), dtype=torch.float32, device=dev)
+
+        def step():
+            for pq, po in packs:
+                tt.int4_gemv(pq, nq, kq, x, out=yq)
+                tt.int4_gemv(po, no, ko, x, out=yo)
+
+        secs = time_steps(torch, step, K, W)
+        per_pair = int4_bytes(nq, kq, 1) + int4_bytes(no, ko, 1)
+        calls = K * copies * 2
+        gbs = per_pair * copies * K / secs / 1e9
+        result = dict(metric="effective HBM GB/s of the grouped affine INT4 GEMV (QKV + O)",
+                      value=round(gbs, 2), unit="GB/s", us_per_call=round(secs / calls * 1e6, 3),
+                      ms_per_step=round(secs / K * 1e3, 4),
+                      config=dict(workload="phi4-14b-int4-qkv-o", qkv=[nq, kq], o=[no, ko],
+                                  group=128, copies_rotated=copies),
+                      roofline=dict(bound="hbm", kernel="k_int4_gemv", achieved=round(gbs, 2),
+                                    peak=PEAK_HBM_GBS, unit="GB/s",
+                                    frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
+
+    elif args.workload == "gptoss":
+        w = workloads.GPTOSS
+        layers, E = w.layers, w.n_experts
+        log(f"setup {w.name}: 1 generated layer of {E} experts, {layers} device copies")
+        gb = workloads.expert_bank(w, 0, "gate")
+        ub = workloads.expert_bank(w, 0, "up")
+        db = workloads.expert_bank(w, 0, "down")
+        gs = tt.mxfp4_gateup_pack_bytes(w.inter, w.hidden)
+        ds = tt.mxfp4_matrix_pack_bytes(w.hidden, w.inter)
+        gu = np.empty(E * gs, np.uint8)
+        dn = np.empty(E * ds, np.uint8)
+        for e in range(E):
+            tt.pack_mxfp4_gateup((gb[0][e], gb[1][e], gb[2][e]), (ub[0][e], ub[1][e], ub[2][e]),
+                                 w.inter, w.hidden, out=gu[e * gs:(e + 1) * gs])
+            tt.pack_mxfp4_matrix(db[0][e], db[1][e], db[2][e], w.hidden, w.inter,
+                                 out=dn[e * ds:(e + 1) * ds])
+        del gb, ub, db
+        gu0 = torch.from_numpy(gu).to(dev)
+        dn0 = torch.from_numpy(dn).to(dev)
+        banks = [(gu0, dn0)] + [(gu0.clone(), dn0.clone()) for _ in range(layers - 1)]
+        nlog = 64
+        logits = [torch.from_numpy(workloads.router_logits(w.wid, s, 1, E).view(np.int16)).to(dev)
+                  for s in range(nlog)]
+        x = torch.from_numpy(workloads.activations(w.wid, 0, 1, w.hidden).view(np.int16)).to(dev)
+        ids = torch.empty((1, w.topk), dtype=torch.int32, device=dev)
+        wt = torch.empty((1, w.topk), dtype=torch.float32, device=dev)
+        h = torch.empty((1, w.topk, w.inter), dtype=torch.bfloat16, device=dev)
+        y = torch.empty((1, w.hidden), dtype=torch.float32, device=dev)
+        state = {"i": 0}
+
+        def step():
+            for li, (g_, d_) in enumerate(banks):
+                tt.moe_route_topk(logits[(state["i"] + li) % nlog], w.topk, ids=ids, w=wt)
+                tt.moe_mxfp4_gateup_swiglu(g_, E, w.inter, w.hidden, x, ids, out=h)
+                tt.moe_mxfp4_down_combine(d_, E, w.hidden, w.inter, h, ids, wt, out=y)
+            state["i"] += 1
+
+        secs = time_steps(torch, step, K, W)
+        per_layer = (w.topk * (2 * mx_matrix_bytes(w.inter, w.hidden)) + w.hidden * 2
+                     + w.topk * w.inter * 2) + (w.topk * mx_matrix_bytes(w.hidden, w.inter)
+                                                + w.topk * w.inter * 2 + w.hidden * 4)
+        gbs = per_layer * layers * K / secs / 1e9
+        result = dict(metric="effective HBM GB/s of the routed-expert MXFP4 layer "
+                             "(route + gate/up SwiGLU + down/combine)",
+                      value=round(gbs, 2), unit="GB/s",
+                      us_per_layer=round(secs / (K * layers) * 1e6, 3),
+                      ms_per_step=round(secs / K * 1e3, 4),
+                      config=dict(workload=w.name, hidden=w.hidden, inter=w.inter, experts=E,
+                                  topk=w.topk, batch=1, layers_rotated=layers, h_dtype="bf16"),
+                      roofline=dict(bound="hbm", kernel="k_gateup_valu+k_down_combine",
+                                    achieved=round(gbs, 2), peak=PEAK_HBM_GBS, unit="GB/s",
+                                    frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
+    else:
+        raise SystemExit(f"unknown workload {args.workload}")
+
+    result.update(n_gpus=1, steps=K, warmup=W, higher_is_better=True, scaling="strong",
+                  vs_baseline=None, dtype="fp4-e2m1 x bf16 -> fp32 accumulate",
+                  data="synthetic (seeded codes, scales, postscales, activations)")
+    if "cpu_baseline" not in result:
+        result["cpu_baseline"] = None
+    order = ["metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+             "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+             "roofline", "cpu_baseline"]
+    out = {k: result[k] for k in order if k in result}
+    out.update({k: v for k, v in result.items() if k not in out})
+    print(json.dumps(out), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="smollm3",
+                    choices=["smollm3", "tiny", "phi4", "phi4-int4", "gptoss", "batched"])
+    ap.add_argument("--batch", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures a single GPU; --gpus {args.gpus} is not supported: the "
+              "projections are measured on one MI355X only.", file=sys.stderr)
+        sys.exit(2)
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

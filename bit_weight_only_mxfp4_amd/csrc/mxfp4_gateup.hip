@@ -1,0 +1,424 @@
+// mxfp4_gateup.hip -- MXFP4 gate/up projection fused with the row postscale
+// and SwiGLU, dense and routed-expert, for gfx950.
+//
+// What is computed ("Dev Log #4", section "Where Blackwell helps": read packed
+// FP4 weights and block scales, multiply against BF16 activations, accumulate
+// safely, then apply the row postscale; "Dev Log #2": gated activation;
+// stardance page, "numerical drift & speedups": the same over the selected
+// experts):  out[r] = silu(ps_g[r] * (Wg x)[r]) * (ps_u[r] * (Wu x)[r]).
+//
+// Batch 1 (and the routed experts, one token per slot) runs on the vector
+// ALUs: one workgroup per 16-row tile (8 gate + 8 up rows of the same output
+// features), KS waves splitting the tile's K units.  Per unit a lane streams
+// 16 code bytes (one 32-element block), converts byte pairs of codes to bf16
+// with the hardware FP4 conversion, takes fp32 dot2 products against the
+// activations staged once in LDS, and scales the block's partial sum by its
+// E8M0 scale.  A cross-lane reduction over the 4 pieces of a row and a
+// fixed-order cross-wave sum give the row dot products; the postscale and
+// SwiGLU run in registers.
+//
+// Batch 2..32 runs on MFMA (v_mfma_f32_16x16x32_bf16): the same 16-byte loads
+// become bf16 A operands with the block scale folded into the conversion,
+// the activations of up to 32 tokens are staged once per workgroup in LDS
+// and feed the B operands, and persistent workgroups walk the tiles.
+#include <algorithm>
+
+#include "device.h"
+#include "tt_internal.h"
+
+namespace tt {
+
+struct GateUpArgs {
+    const uint8_t *w;       // gate/up pack, or the bank base for experts
+    int64_t expert_stride;  // bytes per expert pack
+    int64_t tile_stride;
+    int32_t ntiles;         // tiles per pack
+    int32_t nb, units, qv_last;
+    int32_t scale_off, ps_off;
+    const uint16_t *x;      // [tokens][hidden] bf16
+    int32_t hidden;
+    const int32_t *ids;     // [slots] expert ids, or NULL for the dense call
+    int32_t topk, n_experts;
+    void *out;              // [slots][inter]
+    int32_t out_bf16;
+    int32_t inter;
+    int32_t batch;          // tokens (MFMA path)
+    int32_t ks;             // waves per tile (vector path)
+};
+
+// Tuning of the vector path: units of K per wave (4, 8, 12 or 16) and tiles
+// per workgroup.
+#ifndef TT_GATEUP_UPW
+#define TT_GATEUP_UPW 4
+#endif
+#ifndef TT_GATEUP_TPB
+#define TT_GATEUP_TPB 2
+#endif
+constexpr int kPF = 8;           // units in flight per wave (MFMA path)
+constexpr int kOob = 0x7FFFFF00; // buffer offset past every tile: loads return 0
+
+// Byte offset of lane `lane`'s 16 code bytes in unit kk.  Lanes whose piece
+// lies past the row end (only in the last unit) re-read piece 0 of their row;
+// their activations are zero in LDS and their scale byte is 127, so they add
+// exactly zero.
+__device__ __forceinline__ int code_off(int kk, int lane, int units, int qv_last) {
+    return kk * kUnitBytes +
+           ((kk == units - 1 && (lane >> 4) >= qv_last) ? (lane & 15) * 16 : lane * 16);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, int64_t bytes) {
+    // raw buffer: stride 0, loads at offsets >= bytes return zero
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, int off) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// LDS-only workgroup barrier: orders LDS traffic without waiting for the
+// weight loads still in flight.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Vector path.  Workgroup = TPB tiles x ks waves; wave (t, p) owns units
+// [p * UPW, p * UPW + UPW) of tile blockIdx.x * TPB + t.  Issue order per
+// wave: its share of the activations, then all UPW weight loads and UPW / 4
+// scale dwords.  Loads complete in order, so the activations reach LDS while
+// the weights are still streaming; after an LDS-only barrier each unit is
+// consumed as soon as its load lands.  Units past the end of K, and tiles
+// past the end of the pack, read at an out-of-range buffer offset and get
+// zeros, which contribute exactly nothing.
+template <int UPW, int TPB>
+__global__ __launch_bounds__(512) void k_gateup_valu(GateUpArgs a) {
+    static_assert(UPW % 4 == 0 && UPW <= 16, "units per wave");
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int ks = a.ks;
+    // activations are staged zero-filled up to ks * UPW units, so that the
+    // units past the end of K (zero codes) meet zero activations, never
+    // uninitialised LDS
+    const int xchunks = ks * UPW * 16;
+    uint4 *xs4 = reinterpret_cast<uint4 *>(smem);
+    float *red = reinterpret_cast<float *>(smem + xchunks * 16);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int nthreads = blockDim.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tsub = wave / ks, part = wave - tsub * ks;
+    const int tile = blockIdx.x * TPB + tsub, slot = blockIdx.y;
+
+    const uint8_t *base = a.w;
+    int tok = slot;
+    if (a.ids) {
+        const int e = a.ids[slot];
+        tok = slot / a.topk;
+        if (e < 0 || e >= a.n_experts) {
+            for (int i = tid; i < TPB * 8; i += nthreads) {
+                const int pair = blockIdx.x * TPB * 8 + i;
+                if (pair < a.inter)
+                    store_out(a.out, (int64_t)slot * a.inter + pair, __builtin_nanf(""),
+                              a.out_bf16);
+            }
+            return;
+        }
+        base += (int64_t)e * a.expert_stride;
+    }
+
+    // 1. activations: each thread fetches at most UPW / 4 chunks of 16 bytes
+    constexpr int XC = UPW / 4;  // nthreads * XC >= xchunks
+    const int xvalid = a.hidden / 8;
+    const uint4 *xg = reinterpret_cast<const uint4 *>(a.x + (int64_t)tok * a.hidden);
+    uint4 xv[XC];
+#pragma unroll
+    for (int j = 0; j < XC; ++j) {
+        const int idx = tid + j * nthreads;
+        xv[j] = idx < xvalid ? xg[idx] : make_uint4(0, 0, 0, 0);
+    }
+
+    // 2. weights
+    const bool tile_ok = tile < a.ntiles;
+    const uint8_t *tb = base + (int64_t)(tile_ok ? tile : 0) * a.tile_stride;
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(tb, a.tile_stride);
+    const int q = lane >> 4;
+    const int u0 = part * UPW;
+    const int n = tile_ok ? max(0, min(UPW, a.units - u0)) : 0;
+    uint4 c[UPW];
+    uint32_t sd[UPW / 4];
+    const int voff = u0 * kUnitBytes + lane * 16;
+    const int soff = a.scale_off + (u0 >> 2) * kGroupBytes + lane * 4;
+    // each scale dword goes out just ahead of its four units, so that unit i
+    // only waits for the loads issued before it
+#pragma unroll
+    for (int g = 0; g < UPW / 4; ++g) {
+        sd[g] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * g < n ? soff + g * kGroupBytes : kOob,
+                                                     0, 0);
+#pragma unroll
+        for (int i = 4 * g; i < 4 * g + 4; ++i)
+            c[i] = load16(rs, i < n ? voff + i * kUnitBytes : kOob);
+    }
+
+    // 3. activations to LDS (zero past K), then an LDS-only barrier
+#pragma unroll
+    for (int j = 0; j < XC; ++j) {
+        const int idx = tid + j * nthreads;
+        if (idx < xchunks) xs4[idx] = xv[j];
+    }
+    lds_barrier();
+
+    // 4. consume the units in load order
+    float acc = 0.0f;
+    const uint4 *xb = xs4 + (4 * u0 + q) * 4;
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+        const float p = fp4x32_dot_bf16(c[i], xb + i * 16);
+        const uint32_t e = (sd[i >> 2] >> (8 * (i & 3))) & 255u;
+        acc = fmaf(p, e8m0_f32(e), acc);
+    }
+    // the four pieces of each row -> full row partial (lanes r, r+16, r+32, r+48)
+    acc += __shfl_xor(acc, 16);
+    acc += __shfl_xor(acc, 32);
+    if (TPB * ks > 1) {
+        if (lane < 16) red[wave * 16 + lane] = acc;
+        lds_barrier();
+        if (part != 0) return;
+        if (lane < 16) {
+            acc = red[(tsub * ks) * 16 + lane];
+            for (int w = 1; w < ks; ++w) acc += red[(tsub * ks + w) * 16 + lane];
+        }
+    }
+    if (!tile_ok) return;
+    const float ps = (lane < 16) ? reinterpret_cast<const float *>(tb + a.ps_off)[lane] : 0.0f;
+    const float y = acc * ps;             // tile rows 0..7 gate, 8..15 up
+    const float u = __shfl_down(y, 8);
+    const int pair = tile * 8 + lane;
+    if (lane < 8 && pair < a.inter)
+        store_out(a.out, (int64_t)slot * a.inter + pair, silu(y) * u, a.out_bf16);
+}
+
+// MFMA path.  NCOL column blocks of 16 tokens.  LDS row stride is padded by
+// 16 bytes so the 16 lanes of a B-operand read hit different banks.
+template <int NCOL>
+__global__ __launch_bounds__(512) void k_gateup_mfma(GateUpArgs a) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
+    const int rs = a.units * 128 + 8;  // bf16 elements per token row
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nw = blockDim.x >> 6;
+
+    for (int t = 0; t < a.batch; ++t)
+        stage_bf16(xs + t * rs, a.x + (int64_t)t * a.hidden, a.hidden, a.units * 128, tid,
+                   blockDim.x);
+    __syncthreads();
+
+    const int r = lane & 15, q = lane >> 4;
+    for (int tile = blockIdx.x * nw + wave; tile < a.ntiles; tile += gridDim.x * nw) {
+        const uint8_t *tb = a.w + (int64_t)tile * a.tile_stride;
+        const uint8_t *sp = tb + a.scale_off + lane * 4;
+        f32x4_t C[NCOL];
+#pragma unroll
+        for (int cb = 0; cb < NCOL; ++cb) C[cb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int kb = 0; kb < a.units; kb += kPF) {
+            uint4 c[kPF];
+            uint32_t s[kPF];
+#pragma unroll
+            for (int i = 0; i < kPF; ++i) {
+                const int kk = kb + i;
+                if (kk < a.units) {
+                    c[i] = *reinterpret_cast<const uint4 *>(
+                        tb + code_off(kk, lane, a.units, a.qv_last));
+                    s[i] = *reinterpret_cast<const uint32_t *>(sp + (kk >> 2) * kGroupBytes);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kPF; ++i) {
+                const int kk = kb + i;
+                if (kk < a.units) {
+                    const float sc = e8m0_f32((s[i] >> (8 * (kk & 3))) & 255u);
+                    const uint32_t cw[4] = {c[i].x, c[i].y, c[i].z, c[i].w};
+                    const int kbase = (4 * kk + q) * 32;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const bf16x8_t A = fp4x8_to_bf16x8(cw[j], sc);
+#pragma unroll
+                        for (int cb = 0; cb < NCOL; ++cb) {
+                            const uint4 xb = *reinterpret_cast<const uint4 *>(
+                                xs + (cb * 16 + r) * rs + kbase + 8 * j);
+                            C[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                A, __builtin_bit_cast(bf16x8_t, xb), C[cb], 0, 0, 0);
+                        }
+                    }
+                }
+            }
+        }
+        // lane (token column r, row group q) holds rows 4q..4q+3 of the tile
+        const float4 ps4 = reinterpret_cast<const float4 *>(tb + a.ps_off)[q];
+        const float psv[4] = {ps4.x, ps4.y, ps4.z, ps4.w};
+#pragma unroll
+        for (int cb = 0; cb < NCOL; ++cb) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float y = C[cb][t] * psv[t];
+                const float u = __shfl_down(y, 32);
+                const int token = cb * 16 + r, pair = tile * 8 + 4 * q + t;
+                if (lane < 32 && token < a.batch && pair < a.inter)
+                    store_out(a.out, (int64_t)token * a.inter + pair, silu(y) * u, a.out_bf16);
+            }
+        }
+    }
+}
+
+namespace {
+
+int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cus[dev]) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            v <= 0)
+            v = 256;
+        cus[dev] = v;
+    }
+    return cus[dev];
+}
+
+template <int UPW>
+tt_status launch_valu_upw(GateUpArgs a, int slots, hipStream_t stream) {
+    a.ks = (int32_t)ceil_div(a.units, UPW);
+    const int tpb = (a.ks * TT_GATEUP_TPB <= 8) ? TT_GATEUP_TPB : 1;
+    const size_t lds = (size_t)a.ks * UPW * 256 + (size_t)tpb * a.ks * 64;
+    dim3 grid((unsigned)ceil_div(a.ntiles, tpb), (unsigned)slots);
+    const char *what = "mxfp4 gate/up (vector path)";
+    if (tpb == 1)
+        return launch(what, k_gateup_valu<UPW, 1>, grid, dim3(64 * a.ks), lds, stream, a);
+    return launch(what, k_gateup_valu<UPW, TT_GATEUP_TPB>, grid, dim3(64 * tpb * a.ks), lds,
+                  stream, a);
+}
+
+// Units per wave: the tuned target, raised until a tile needs at most 8 waves
+// (K <= 16384 gives at most 128 units, so 16 units per wave always suffice).
+tt_status launch_valu(GateUpArgs a, int slots, hipStream_t stream) {
+    int upw = TT_GATEUP_UPW;
+    while (ceil_div(a.units, upw) > 8) upw += 4;
+    switch (upw) {
+        case 4: return launch_valu_upw<4>(a, slots, stream);
+        case 8: return launch_valu_upw<8>(a, slots, stream);
+        case 12: return launch_valu_upw<12>(a, slots, stream);
+        case 16: return launch_valu_upw<16>(a, slots, stream);
+        default: return fail(TT_E_SHAPE, "hidden = %d needs more than 8 waves per tile", a.hidden);
+    }
+}
+
+constexpr size_t kMaxLds = 160 * 1024;
+
+size_t mfma_lds(const GateUpArgs &a, int ncol) {
+    return (size_t)ncol * 16 * ((size_t)a.units * 128 + 8) * 2;
+}
+
+template <int NCOL>
+tt_status launch_mfma(const GateUpArgs &a, hipStream_t stream) {
+    const size_t lds = mfma_lds(a, NCOL);
+    static bool attr_set[64] = {false};
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (lds > 64 * 1024 && dev >= 0 && dev < 64 && !attr_set[dev]) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(k_gateup_mfma<NCOL>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)kMaxLds) != hipSuccess)
+            return fail(TT_E_HIP, "cannot raise the LDS limit of the MFMA gate/up kernel");
+        attr_set[dev] = true;
+    }
+    const int per_cu = (int)(kMaxLds / lds);
+    const int waves = 8;
+    int blocks = (int)ceil_div(a.ntiles, waves);
+    blocks = min(blocks, device_cus() * max(per_cu, 1));
+    return launch("mxfp4 gate/up (MFMA path)", k_gateup_mfma<NCOL>, dim3(blocks),
+                  dim3(64 * waves), lds, stream, a);
+}
+
+GateUpArgs make_args(const void *w, int64_t inter, int64_t hidden, const void *x,
+                     void *out, int32_t out_dtype) {
+    const MxGeom g = mx_geom(hidden);
+    GateUpArgs a;
+    a.w = static_cast<const uint8_t *>(w);
+    a.expert_stride = ceil_div(inter, kTileRows / 2) * g.stride;
+    a.tile_stride = g.stride;
+    a.ntiles = (int32_t)ceil_div(inter, kTileRows / 2);
+    a.nb = (int32_t)g.nb;
+    a.units = (int32_t)g.units;
+    a.qv_last = (int32_t)g.qv_last;
+    a.scale_off = (int32_t)g.scale_off;
+    a.ps_off = (int32_t)g.ps_off;
+    a.x = static_cast<const uint16_t *>(x);
+    a.hidden = (int32_t)hidden;
+    a.ids = nullptr;
+    a.topk = 1;
+    a.n_experts = 1;
+    a.out = out;
+    a.out_bf16 = out_dtype == TT_BF16;
+    a.inter = (int32_t)inter;
+    a.batch = 1;
+    return a;
+}
+
+tt_status check_gateup_common(const void *w, int64_t inter, int64_t hidden, const void *x,
+                              int64_t batch, void *out, int32_t out_dtype) {
+    TT_TRY(check_ptr(w, "w_gu"));
+    TT_TRY(check_ptr(x, "x"));
+    TT_TRY(check_ptr(out, "out"));
+    TT_TRY(check_range(inter, 1, TT_MAX_ROWS, "inter"));
+    TT_TRY(check_range(hidden, 32, TT_MAX_K, "hidden"));
+    if (hidden % 32) return fail(TT_E_SHAPE, "hidden = %lld is not a multiple of 32", (long long)hidden);
+    TT_TRY(check_range(batch, 1, TT_MAX_BATCH, "batch"));
+    TT_TRY(check_dtype(out_dtype, "out_dtype"));
+    TT_TRY(check_align(w, 16, "w_gu"));
+    TT_TRY(check_align(x, 16, "x"));
+    TT_TRY(check_align(out, out_dtype == TT_F32 ? 4 : 2, "out"));
+    return TT_OK;
+}
+
+}  // namespace
+}  // namespace tt
+
+using namespace tt;
+
+extern "C" tt_status tt_mxfp4_gateup_swiglu(const void *w_gu, int64_t inter, int64_t hidden,
+                                            const void *x, int64_t batch, void *out,
+                                            int32_t out_dtype, void *stream) {
+    TT_TRY(check_gateup_common(w_gu, inter, hidden, x, batch, out, out_dtype));
+    GateUpArgs a = make_args(w_gu, inter, hidden, x, out, out_dtype);
+    a.batch = (int32_t)batch;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    tt_status st;
+    if (batch == 1)
+        st = launch_valu(a, 1, s);
+    else if (batch <= 16 && mfma_lds(a, 1) <= kMaxLds)
+        st = launch_mfma<1>(a, s);
+    else if (mfma_lds(a, 2) <= kMaxLds)
+        st = launch_mfma<2>(a, s);
+    else
+        st = launch_valu(a, (int)batch, s);  // one weight pass per token
+    if (st == TT_OK) clear_error();
+    return st;
+}
+
+extern "C" tt_status tt_moe_mxfp4_gateup_swiglu(const void *bank, int64_t n_experts,
+                                                int64_t inter, int64_t hidden, const void *x,
+                                                int64_t batch, const int32_t *ids, int64_t topk,
+                                                void *h, int32_t h_dtype, void *stream) {
+    TT_TRY(check_gateup_common(bank, inter, hidden, x, batch, h, h_dtype));
+    TT_TRY(check_ptr(ids, "ids"));
+    TT_TRY(check_align(ids, 4, "ids"));
+    TT_TRY(check_range(n_experts, 1, TT_MAX_EXPERTS, "n_experts"));
+    TT_TRY(check_range(topk, 1, n_experts < TT_MAX_TOPK ? n_experts : TT_MAX_TOPK, "topk"));
+    GateUpArgs a = make_args(bank, inter, hidden, x, h, h_dtype);
+    a.ids = ids;
+    a.topk = (int32_t)topk;
+    a.n_experts = (int32_t)n_experts;
+    tt_status st = launch_valu(a, (int)(batch * topk), static_cast<hipStream_t>(stream));
+    if (st == TT_OK) clear_error();
+    return st;
+}

@@ -1,0 +1,298 @@
+// pack.cpp -- host-side packers (canonical -> tiled device layout) and the
+// affine INT4 quantizer.  Pure CPU code, caller-owned buffers.
+#include <math.h>
+#include <string.h>
+
+#include "layout.h"
+#include "tt_internal.h"
+
+namespace tt {
+namespace {
+
+// Write one MXFP4 tile.  crow/srow[r] point at canonical row r of the tile
+// (NULL for a padding row); ps[r] is its postscale.
+void pack_mx_tile(const MxGeom &g, const uint8_t *const crow[kTileRows],
+                  const uint8_t *const srow[kTileRows],
+                  const float ps[kTileRows], uint8_t *dst) {
+    for (int64_t kk = 0; kk < g.units; ++kk) {
+        int64_t qv = (kk == g.units - 1) ? g.qv_last : 4;
+        for (int64_t q = 0; q < qv; ++q) {
+            int64_t blk = 4 * kk + q;
+            for (int r = 0; r < kTileRows; ++r) {
+                uint8_t *o = dst + kUnitBytes * kk + 16 * (r + 16 * q);
+                if (crow[r])
+                    memcpy(o, crow[r] + 16 * blk, 16);
+                else
+                    memset(o, 0, 16);
+            }
+        }
+    }
+    uint8_t *sc = dst + g.scale_off;
+    for (int64_t j = 0; j < g.groups; ++j) {
+        for (int lane = 0; lane < 64; ++lane) {
+            int r = lane % 16, q = lane / 16;
+            for (int t = 0; t < 4; ++t) {
+                int64_t kk = 4 * j + t, blk = 4 * kk + q;
+                uint8_t e = kPadScale;
+                if (kk < g.units && blk < g.nb && srow[r]) e = srow[r][blk];
+                sc[kGroupBytes * j + 4 * lane + t] = e;
+            }
+        }
+    }
+    uint8_t *tr = dst + g.ps_off;
+    memcpy(tr, ps, sizeof(float) * kTileRows);
+    memset(tr + sizeof(float) * kTileRows, 0, kTrailerBytes - sizeof(float) * kTileRows);
+}
+
+tt_status check_mx_shape(int64_t n, int64_t k, const char *nname) {
+    TT_TRY(check_range(n, 1, TT_MAX_ROWS, nname));
+    TT_TRY(check_range(k, 32, TT_MAX_K, "k"));
+    if (k % 32) return fail(TT_E_SHAPE, "k = %lld is not a multiple of 32", (long long)k);
+    return TT_OK;
+}
+
+// Round an fp64 value to the nearest binary16 (ties to even) and return the
+// bit pattern.  Works on the binary64 fields directly.
+uint16_t f16_bits_from_f64(double v) {
+    uint64_t b;
+    memcpy(&b, &v, sizeof b);
+    uint16_t sign = static_cast<uint16_t>((b >> 48) & 0x8000);
+    int bexp = static_cast<int>((b >> 52) & 0x7FF);
+    uint64_t man = b & ((1ull << 52) - 1);
+    if (bexp == 0x7FF) return sign | (man ? 0x7E00 : 0x7C00);
+    if (bexp == 0) return sign;  // binary64 subnormals are far below 2^-25
+    int e = bexp - 1023;
+    if (e > 15) return sign | 0x7C00;
+    uint64_t sig = man | (1ull << 52);
+    int shift = (e >= -14) ? 42 : 42 + (-14 - e);
+    if (shift >= 60) return sign;
+    uint64_t kept = sig >> shift;
+    uint64_t rem = sig & ((1ull << shift) - 1);
+    uint64_t half = 1ull << (shift - 1);
+    if (rem > half || (rem == half && (kept & 1))) ++kept;
+    if (e < -14) return static_cast<uint16_t>(sign | kept);  // 1024 is 2^-14
+    int E = e + 15;
+    if (kept == 2048) {
+        kept = 1024;
+        ++E;
+    }
+    if (E >= 31) return sign | 0x7C00;
+    return static_cast<uint16_t>(sign | (E << 10) | (kept - 1024));
+}
+
+double f16_bits_to_f64(uint16_t h) {
+    int E = (h >> 10) & 31, F = h & 1023;
+    double m = (E == 0) ? ldexp(static_cast<double>(F), -24)
+                        : ldexp(static_cast<double>(1024 + F), E - 25);
+    return (h & 0x8000) ? -m : m;
+}
+
+}  // namespace
+}  // namespace tt
+
+using namespace tt;
+
+extern "C" {
+
+int64_t tt_mxfp4_matrix_pack_bytes(int64_t n, int64_t k) {
+    tt_status st = check_mx_shape(n, k, "n");
+    if (st != TT_OK) return st;
+    return ceil_div(n, kTileRows) * mx_geom(k).stride;
+}
+
+int64_t tt_mxfp4_gateup_pack_bytes(int64_t inter, int64_t hidden) {
+    tt_status st = check_mx_shape(inter, hidden, "inter");
+    if (st != TT_OK) return st;
+    return ceil_div(inter, kTileRows / 2) * mx_geom(hidden).stride;
+}
+
+tt_status tt_pack_mxfp4_matrix(const uint8_t *codes, const uint8_t *scales,
+                               const float *ps, int64_t n, int64_t k,
+                               void *dst, int64_t dst_bytes) {
+    TT_TRY(check_ptr(codes, "codes"));
+    TT_TRY(check_ptr(scales, "scales"));
+    TT_TRY(check_ptr(dst, "dst"));
+    TT_TRY(check_mx_shape(n, k, "n"));
+    const MxGeom g = mx_geom(k);
+    const int64_t tiles = ceil_div(n, kTileRows);
+    if (dst_bytes < tiles * g.stride)
+        return fail(TT_E_SIZE, "dst holds %lld bytes, the pack needs %lld",
+                    (long long)dst_bytes, (long long)(tiles * g.stride));
+    uint8_t *out = static_cast<uint8_t *>(dst);
+    for (int64_t t = 0; t < tiles; ++t) {
+        const uint8_t *crow[kTileRows], *srow[kTileRows];
+        float p[kTileRows];
+        for (int r = 0; r < kTileRows; ++r) {
+            int64_t row = t * kTileRows + r;
+            bool ok = row < n;
+            crow[r] = ok ? codes + row * (k / 2) : nullptr;
+            srow[r] = ok ? scales + row * (k / 32) : nullptr;
+            p[r] = ok ? (ps ? ps[row] : 1.0f) : 0.0f;
+        }
+        pack_mx_tile(g, crow, srow, p, out + t * g.stride);
+    }
+    clear_error();
+    return TT_OK;
+}
+
+tt_status tt_pack_mxfp4_gateup(const uint8_t *g_codes, const uint8_t *g_scales,
+                               const float *g_ps,
+                               const uint8_t *u_codes, const uint8_t *u_scales,
+                               const float *u_ps,
+                               int64_t inter, int64_t hidden,
+                               void *dst, int64_t dst_bytes) {
+    TT_TRY(check_ptr(g_codes, "g_codes"));
+    TT_TRY(check_ptr(g_scales, "g_scales"));
+    TT_TRY(check_ptr(u_codes, "u_codes"));
+    TT_TRY(check_ptr(u_scales, "u_scales"));
+    TT_TRY(check_ptr(dst, "dst"));
+    TT_TRY(check_mx_shape(inter, hidden, "inter"));
+    const MxGeom g = mx_geom(hidden);
+    const int64_t tiles = ceil_div(inter, kTileRows / 2);
+    if (dst_bytes < tiles * g.stride)
+        return fail(TT_E_SIZE, "dst holds %lld bytes, the pack needs %lld",
+                    (long long)dst_bytes, (long long)(tiles * g.stride));
+    uint8_t *out = static_cast<uint8_t *>(dst);
+    for (int64_t t = 0; t < tiles; ++t) {
+        const uint8_t *crow[kTileRows], *srow[kTileRows];
+        float p[kTileRows];
+        for (int i = 0; i < kTileRows / 2; ++i) {
+            int64_t row = t * (kTileRows / 2) + i;
+            bool ok = row < inter;
+            crow[i] = ok ? g_codes + row * (hidden / 2) : nullptr;
+            srow[i] = ok ? g_scales + row * (hidden / 32) : nullptr;
+            p[i] = ok ? (g_ps ? g_ps[row] : 1.0f) : 0.0f;
+            crow[i + 8] = ok ? u_codes + row * (hidden / 2) : nullptr;
+            srow[i + 8] = ok ? u_scales + row * (hidden / 32) : nullptr;
+            p[i + 8] = ok ? (u_ps ? u_ps[row] : 1.0f) : 0.0f;
+        }
+        pack_mx_tile(g, crow, srow, p, out + t * g.stride);
+    }
+    clear_error();
+    return TT_OK;
+}
+
+tt_status tt_quantize_int4_affine(const float *w, int64_t n, int64_t k,
+                                  int64_t group, uint8_t *q, uint16_t *s,
+                                  uint16_t *z) {
+    TT_TRY(check_ptr(w, "w"));
+    TT_TRY(check_ptr(q, "q"));
+    TT_TRY(check_ptr(s, "s"));
+    TT_TRY(check_ptr(z, "z"));
+    TT_TRY(check_range(n, 1, TT_MAX_ROWS, "n"));
+    TT_TRY(check_range(k, 2, TT_MAX_K, "k"));
+    if (k % 2) return fail(TT_E_SHAPE, "k = %lld is odd", (long long)k);
+    if (group != TT_INT4_GROUP)
+        return fail(TT_E_SHAPE, "group = %lld; only %d is supported", (long long)group,
+                    TT_INT4_GROUP);
+    const int64_t G = ceil_div(k, group);
+    // Check every scale first so that nothing is written on TT_E_RANGE.
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t gi = 0; gi < G; ++gi) {
+            const float *row = w + r * k;
+            int64_t a = gi * group, b = a + group < k ? a + group : k;
+            double lo = 0.0, hi = 0.0;
+            for (int64_t j = a; j < b; ++j) {
+                double v = row[j];
+                lo = v < lo ? v : lo;
+                hi = v > hi ? v : hi;
+            }
+            uint16_t sb = f16_bits_from_f64((hi - lo) / 15.0);
+            if ((sb & 0x7C00) == 0x7C00)
+                return fail(TT_E_RANGE, "row %lld group %lld: scale %g overflows binary16",
+                            (long long)r, (long long)gi, (hi - lo) / 15.0);
+        }
+    for (int64_t r = 0; r < n; ++r) {
+        const float *row = w + r * k;
+        uint8_t *qrow = q + r * (k / 2);
+        memset(qrow, 0, static_cast<size_t>(k / 2));
+        for (int64_t gi = 0; gi < G; ++gi) {
+            int64_t a = gi * group, b = a + group < k ? a + group : k;
+            double lo = 0.0, hi = 0.0;
+            for (int64_t j = a; j < b; ++j) {
+                double v = row[j];
+                lo = v < lo ? v : lo;
+                hi = v > hi ? v : hi;
+            }
+            uint16_t sb = f16_bits_from_f64((hi - lo) / 15.0);
+            double sv = f16_bits_to_f64(sb);
+            if (sv == 0.0) {
+                sb = 0x3C00;
+                sv = 1.0;
+            }
+            double zv = nearbyint(-lo / sv);
+            zv = zv < 0.0 ? 0.0 : (zv > 15.0 ? 15.0 : zv);
+            s[r * G + gi] = sb;
+            z[r * G + gi] = f16_bits_from_f64(zv);
+            for (int64_t j = a; j < b; ++j) {
+                double qv = nearbyint(static_cast<double>(row[j]) / sv) + zv;
+                qv = qv < 0.0 ? 0.0 : (qv > 15.0 ? 15.0 : qv);
+                uint8_t c = static_cast<uint8_t>(qv);
+                qrow[j >> 1] |= (j & 1) ? static_cast<uint8_t>(c << 4) : c;
+            }
+        }
+    }
+    clear_error();
+    return TT_OK;
+}
+
+int64_t tt_int4_pack_bytes(int64_t n, int64_t k, int64_t group) {
+    tt_status st = check_range(n, 1, TT_MAX_ROWS, "n");
+    if (st == TT_OK) st = check_range(k, 2, TT_MAX_K, "k");
+    if (st != TT_OK) return st;
+    if (k % 2) return fail(TT_E_SHAPE, "k = %lld is odd", (long long)k);
+    if (group != TT_INT4_GROUP)
+        return fail(TT_E_SHAPE, "group = %lld; only %d is supported", (long long)group,
+                    TT_INT4_GROUP);
+    return ceil_div(n, kTileRows) * i4_geom(k).stride;
+}
+
+tt_status tt_pack_int4(const uint8_t *q, const uint16_t *s, const uint16_t *z,
+                       int64_t n, int64_t k, int64_t group, void *dst,
+                       int64_t dst_bytes) {
+    TT_TRY(check_ptr(q, "q"));
+    TT_TRY(check_ptr(s, "s"));
+    TT_TRY(check_ptr(z, "z"));
+    TT_TRY(check_ptr(dst, "dst"));
+    int64_t need = tt_int4_pack_bytes(n, k, group);
+    if (need < 0) return static_cast<tt_status>(need);
+    if (dst_bytes < need)
+        return fail(TT_E_SIZE, "dst holds %lld bytes, the pack needs %lld",
+                    (long long)dst_bytes, (long long)need);
+    const I4Geom g = i4_geom(k);
+    const int64_t G = ceil_div(k, group), rowbytes = k / 2;
+    const int64_t tiles = ceil_div(n, kTileRows);
+    uint8_t *out = static_cast<uint8_t *>(dst);
+    for (int64_t t = 0; t < tiles; ++t) {
+        uint8_t *tb = out + t * g.stride;
+        for (int64_t kk = 0; kk < g.units; ++kk) {
+            int64_t qv = (kk == g.units - 1) ? g.qv_last : 4;
+            for (int64_t qq = 0; qq < qv; ++qq) {
+                int64_t piece = 4 * kk + qq;
+                for (int r = 0; r < kTileRows; ++r) {
+                    int64_t row = t * kTileRows + r;
+                    uint8_t *o = tb + kUnitBytes * kk + 16 * (r + 16 * qq);
+                    memset(o, 0, 16);
+                    if (row >= n) continue;
+                    int64_t b0 = 16 * piece, b1 = b0 + 16 < rowbytes ? b0 + 16 : rowbytes;
+                    if (b1 > b0) memcpy(o, q + row * rowbytes + b0, static_cast<size_t>(b1 - b0));
+                }
+            }
+        }
+        uint8_t *sz = tb + g.sz_off;
+        for (int64_t j = 0; j < g.groups; ++j)
+            for (int r = 0; r < kTileRows; ++r)
+                for (int tt_ = 0; tt_ < 4; ++tt_) {
+                    int64_t row = t * kTileRows + r, gi = 4 * j + tt_;
+                    uint32_t v = 0;
+                    if (row < n && gi < G)
+                        v = static_cast<uint32_t>(s[row * G + gi]) |
+                            (static_cast<uint32_t>(z[row * G + gi]) << 16);
+                    memcpy(sz + kGroupBytes * j + 16 * r + 4 * tt_, &v, 4);
+                }
+    }
+    clear_error();
+    return TT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,184 @@
+"""Host-side tests of libtt.so (no GPU): exported symbols, status codes,
+packers and the INT4 quantizer."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_weight_only_mxfp4_amd as tt
+import oracle
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "tt.h")).read()
+    return sorted(set(re.findall(r"\b(tt_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 19
+    lib = ctypes.CDLL(tt.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(tt.EXPORTS)
+
+
+def test_format_info_is_honest():
+    assert tt.format_info(tt.TT_FMT_MXFP4) == dict(bits=4, group=32, scale_kind=0, has_zero=0)
+    assert tt.format_info(tt.TT_FMT_INT4_AFFINE) == dict(bits=4, group=128, scale_kind=1,
+                                                         has_zero=1)
+    with pytest.raises(tt.TTError) as e:
+        tt.format_info(7)
+    assert e.value.status == -4
+
+
+# Fake but aligned non-null device pointers: validation must reject the call
+# before anything touches the device.
+P = ctypes.c_void_p(0x10000)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 16, 64, P, 1, P, 0, None), -1),      # null weights
+    ((P, 16, 48, P, 1, P, 0, None), -2),         # hidden not a multiple of 32
+    ((P, 16, 64, P, 0, P, 0, None), -2),         # batch 0
+    ((P, 16, 64, P, 33, P, 0, None), -2),        # batch > 32
+    ((P, 0, 64, P, 1, P, 0, None), -2),          # no rows
+    ((P, 16, 32768, P, 1, P, 0, None), -2),      # hidden too large
+    ((P, 16, 64, P, 1, P, 5, None), -4),         # bad dtype
+    ((ctypes.c_void_p(0x10008), 16, 64, P, 1, P, 0, None), -3),  # misaligned weights
+])
+def test_gateup_validation(args, status):
+    assert tt.lib.tt_mxfp4_gateup_swiglu(*args) == status
+    assert tt.lib.tt_last_error().decode()
+
+
+def test_moe_and_int4_validation():
+    L = tt.lib
+    assert L.tt_moe_route_topk(P, 1, 32, 9, P, P, None) == -2        # topk > 8
+    assert L.tt_moe_route_topk(P, 1, 3, 4, P, P, None) == -2         # topk > n_experts
+    assert L.tt_moe_route_topk(P, 1, 300, 4, P, P, None) == -2       # too many experts
+    assert L.tt_moe_mxfp4_gateup_swiglu(P, 32, 64, 64, P, 1, None, 4, P, 0, None) == -1
+    assert L.tt_moe_mxfp4_down_combine(P, 32, 64, 48, P, 0, P, P, 1, 4, P, 0, None) == -2
+    assert L.tt_moe_mxfp4_down_combine(P, 32, 64, 64, P, 3, P, P, 1, 4, P, 0, None) == -4
+    assert L.tt_int4_gemv(P, 16, 129, 128, P, 1, P, 0, None) == -2   # odd k
+    assert L.tt_int4_gemv(P, 16, 128, 64, P, 1, P, 0, None) == -2    # group != 128
+    assert L.tt_mxfp4_gateup_dequantize(P, 8, 64, None, None, None, None, None) == -1
+
+
+def test_pack_sizes_and_size_errors():
+    assert tt.mxfp4_gateup_pack_bytes(11008, 2048) == 1376 * (8 * 2048 + 256 * 4 + 128)
+    assert tt.mxfp4_matrix_pack_bytes(2880, 2880) == 180 * (8 * 2880 + 256 * 6 + 128)
+    assert tt.int4_pack_bytes(7680, 5120) == 7680 * 5120 // 2 + 7680 * 40 * 4
+    with pytest.raises(tt.TTError):
+        tt.mxfp4_gateup_pack_bytes(16, 33)
+    g, u = workloads.gateup(workloads.TINY)
+    small = np.empty(100, np.uint8)
+    with pytest.raises(tt.TTError) as e:
+        tt.pack_mxfp4_gateup(g, u, 512, 256, out=small)
+    assert e.value.status == -5
+
+
+def _unpack_mx(packed, nrows_tiles, k):
+    """Read the documented tiled layout back into canonical arrays (tile row
+    order): codes [16T][k/2], scales [16T][k/32], ps [16T]."""
+    nb = k // 32
+    units = -(-nb // 4)
+    qv_last = nb - 4 * (units - 1)
+    groups = -(-units // 4)
+    scale_off = 256 * nb
+    ps_off = scale_off + 256 * groups
+    stride = ps_off + 128
+    T = nrows_tiles
+    codes = np.zeros((16 * T, k // 2), np.uint8)
+    scales = np.zeros((16 * T, nb), np.uint8)
+    ps = np.zeros(16 * T, np.float32)
+    for t in range(T):
+        tb = packed[t * stride:(t + 1) * stride]
+        for kk in range(units):
+            qv = qv_last if kk == units - 1 else 4
+            for q in range(qv):
+                blk = 4 * kk + q
+                for r in range(16):
+                    lane = r + 16 * q
+                    codes[16 * t + r, 16 * blk:16 * blk + 16] = tb[1024 * kk + 16 * lane:
+                                                                   1024 * kk + 16 * lane + 16]
+                    scales[16 * t + r, blk] = tb[scale_off + 256 * (kk // 4) + 4 * lane + kk % 4]
+        ps[16 * t:16 * t + 16] = tb[ps_off:ps_off + 64].view(np.float32)
+    return codes, scales, ps
+
+
+@pytest.mark.parametrize("n,k", [(40, 256), (16, 2880), (5, 96)])
+def test_matrix_pack_follows_documented_layout(n, k):
+    c, s, p = workloads.mxfp4_matrix(9, 0, n, k)
+    packed = tt.pack_mxfp4_matrix(c, s, p, n, k)
+    T = -(-n // 16)
+    uc, us, up = _unpack_mx(packed, T, k)
+    assert np.array_equal(uc[:n], c) and np.array_equal(us[:n], s) and np.array_equal(up[:n], p)
+    assert not uc[n:].any() and np.all(us[n:] == 127)
+
+
+def test_gateup_pack_interleaves_gate_and_up():
+    w = workloads.Workload(9, "t", 160, 20)
+    g, u = workloads.gateup(w)
+    packed = tt.pack_mxfp4_gateup(g, u, w.inter, w.hidden)
+    uc, us, up = _unpack_mx(packed, 3, w.hidden)
+    for t in range(3):
+        for i in range(8):
+            row = 8 * t + i
+            if row >= w.inter:
+                continue
+            assert np.array_equal(uc[16 * t + i], g[0][row])
+            assert np.array_equal(uc[16 * t + 8 + i], u[0][row])
+            assert np.array_equal(us[16 * t + 8 + i], u[1][row])
+            assert up[16 * t + i] == g[2][row] and up[16 * t + 8 + i] == u[2][row]
+
+
+@pytest.mark.parametrize("n,k", [(64, 5120), (40, 200), (9, 328), (3, 2)])
+def test_int4_quantizer_matches_oracle_bit_for_bit(n, k):
+    w = workloads.int4_source(2, 0, n, k)
+    w[0, : min(128, k)] = 0.0
+    q1, s1, z1 = tt.quantize_int4_affine(w)
+    q2, s2, z2 = oracle.int4_quantize(w, 128)
+    assert np.array_equal(q1, q2) and np.array_equal(s1, s2) and np.array_equal(z1, z2)
+
+
+def test_int4_quantizer_range_error_writes_nothing():
+    w = np.array([[-1e6, 1e6]], np.float32)
+    with pytest.raises(tt.TTError) as e:
+        tt.quantize_int4_affine(w)
+    assert e.value.status == -6
+
+
+def test_int4_pack_layout():
+    n, k = 20, 200
+    w = workloads.int4_source(2, 0, n, k)
+    q, s, z = oracle.int4_quantize(w, 128)
+    packed = tt.pack_int4(q, s, z, n, k)
+    nq = -(-k // 32)
+    units = -(-nq // 4)
+    sz_off = 256 * nq
+    stride = sz_off + 256 * (-(-units // 4))
+    assert packed.size == 2 * stride
+    for t in range(2):
+        tb = packed[t * stride:(t + 1) * stride]
+        for r in range(16):
+            row = 16 * t + r
+            for kk in range(units):
+                v = tb[sz_off + 256 * (kk // 4) + 16 * r + 4 * (kk % 4):][:4].view(np.uint32)[0]
+                if row < n:
+                    assert v == (int(s[row, kk]) | (int(z[row, kk]) << 16))
+                else:
+                    assert v == 0
+            for p in range(nq):
+                kk, qq = divmod(p, 4)
+                got = tb[1024 * kk + 16 * (r + 16 * qq):][:16]
+                if row < n:
+                    want = np.zeros(16, np.uint8)
+                    seg = q[row, 16 * p:16 * p + 16]
+                    want[:seg.size] = seg
+                    assert np.array_equal(got, want)

@@ -1,0 +1,184 @@
+"""GPU parity of the MXFP4 gate/up SwiGLU path (dense, batch 1..32) and of the
+MXFP4 decode, against the CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import bit_weight_only_mxfp4_amd as tt
+import oracle
+import workloads
+from _parity import (assert_parity, dev_bf16, dev_u8, h_tol, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+def _f32_bits(a):
+    return np.ascontiguousarray(a, np.float32).view(np.uint32)
+
+
+def _sample_rows(inter, n_random, seed):
+    gen = np.random.default_rng(seed)
+    rows = set(range(min(16, inter))) | set(range(max(0, inter - 16), inter))
+    rows |= set(gen.choice(inter, size=min(n_random, inter), replace=False).tolist())
+    return np.array(sorted(rows), np.int64)
+
+
+def _gateup_case(dev, w, layer, batch, rows=None, out_dtype=torch.float32, g=None, u=None,
+                 x=None):
+    if g is None:
+        g, u = workloads.gateup(w, layer)
+    if x is None:
+        x = workloads.activations(w.wid, layer, batch, w.hidden)
+    packed = dev_u8(tt.pack_mxfp4_gateup(g, u, w.inter, w.hidden), dev)
+    h = tt.mxfp4_gateup_swiglu(packed, w.inter, w.hidden, dev_bf16(x, dev), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    got = to_np(h)
+    ref = oracle.mxfp4_gateup_swiglu(g, u, w.inter, w.hidden, x, rows=rows)
+    if rows is not None:
+        got = got[:, rows]
+    return got, ref
+
+
+# ---- decode, bit-exact --------------------------------------------------------
+
+@pytest.mark.parametrize("n,k", [(40, 256), (33, 2880), (16, 96), (7, 32)])
+def test_mxfp4_dequantize_bit_exact_all_scale_bytes(dev, n, k):
+    gen = np.random.default_rng([n, k])
+    codes = gen.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    scales = gen.integers(0, 256, (n, k // 32), dtype=np.uint8)
+    flat = scales.reshape(-1)
+    flat[: min(256, flat.size)] = np.arange(min(256, flat.size), dtype=np.uint8)
+    ps = gen.uniform(0.5, 1.5, n).astype(np.float32)
+    packed = dev_u8(tt.pack_mxfp4_matrix(codes, scales, ps, n, k), dev)
+    w, p = tt.mxfp4_dequantize(packed, n, k)
+    torch.cuda.synchronize()
+    got = w.cpu().numpy()
+    ref = oracle.mxfp4_dequantize(codes, scales, n, k)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(_f32_bits(got)[~nan], _f32_bits(ref)[~nan])
+    assert np.array_equal(p.cpu().numpy(), ps)
+
+
+def test_mxfp4_every_code_times_every_scale(dev):
+    """Row e holds every code twice under scale byte e: 256 x 16 pairs."""
+    n, k = 256, 32
+    codes = np.tile(np.array([c | (c << 4) for c in range(16)], np.uint8), (n, 1))
+    scales = np.arange(256, dtype=np.uint8).reshape(n, 1)
+    packed = dev_u8(tt.pack_mxfp4_matrix(codes, scales, None, n, k), dev)
+    w, _ = tt.mxfp4_dequantize(packed, n, k)
+    got = w.cpu().numpy()
+    for e in range(256):
+        for c in range(16):
+            want = oracle.mxfp4_weight(c, e)
+            for j in (2 * c, 2 * c + 1):
+                if np.isnan(want):
+                    assert np.isnan(got[e, j])
+                else:
+                    assert _f32_bits(got[e, j]) == _f32_bits(want), (e, c)
+
+
+def test_gateup_dequantize_bit_exact(dev):
+    w = workloads.Workload(9, "t", 2880, 100)
+    g, u = workloads.gateup(w)
+    packed = dev_u8(tt.pack_mxfp4_gateup(g, u, w.inter, w.hidden), dev)
+    gd, ud, gp, up = tt.mxfp4_gateup_dequantize(packed, w.inter, w.hidden)
+    for (c, s, p), d, dp in ((g, gd, gp), (u, ud, up)):
+        ref = oracle.mxfp4_dequantize(c, s, w.inter, w.hidden)
+        assert np.array_equal(_f32_bits(d.cpu().numpy()), _f32_bits(ref))
+        assert np.array_equal(dp.cpu().numpy(), p)
+
+
+# ---- gate/up SwiGLU -------------------------------------------------------------
+
+def test_tiny_config_full(dev):
+    w = workloads.TINY
+    got, ref = _gateup_case(dev, w, 0, 1)
+    assert_parity(got, ref["h"], h_tol(ref), "tiny h256 i512 b1")
+
+
+@pytest.mark.parametrize("hidden,inter", [(32, 8), (96, 100), (2880, 37), (160, 1), (5120, 24),
+                                          (2880, 1024), (3200, 520), (2336, 1000), (16384, 40)])
+def test_ragged_shapes(dev, hidden, inter):
+    w = workloads.Workload(9, "ragged", hidden, inter)
+    got, ref = _gateup_case(dev, w, 0, 1)
+    assert_parity(got, ref["h"], h_tol(ref), f"ragged h{hidden} i{inter}")
+
+
+def test_smollm3_all_layers_sampled_rows(dev):
+    w = workloads.SMOLLM3
+    for layer in range(w.layers):
+        rows = _sample_rows(w.inter, 96, layer)
+        got, ref = _gateup_case(dev, w, layer, 1, rows=rows)
+        assert_parity(got, ref["h"], h_tol(ref), f"smollm3 layer {layer} ({rows.size} rows)")
+
+
+def test_smollm3_layer0_every_row(dev):
+    w = workloads.SMOLLM3
+    got, ref = _gateup_case(dev, w, 0, 1)
+    assert_parity(got, ref["h"], h_tol(ref), "smollm3 layer 0 all rows")
+
+
+def test_phi4_gateup_sampled_rows(dev):
+    w = workloads.PHI4
+    rows = _sample_rows(w.inter, 256, 1)
+    got, ref = _gateup_case(dev, w, 0, 1, rows=rows)
+    assert_parity(got, ref["h"], h_tol(ref), "phi4 gate/up")
+
+
+@pytest.mark.parametrize("batch", [2, 4, 8, 16, 17, 32])
+def test_batched_smollm3_sampled_rows(dev, batch):
+    w = workloads.BATCHED
+    rows = _sample_rows(w.inter, 64, batch)
+    got, ref = _gateup_case(dev, w, 0, batch, rows=rows)
+    assert_parity(got, ref["h"], h_tol(ref), f"batched b{batch}")
+
+
+@pytest.mark.parametrize("batch", [1, 8])
+def test_bf16_output(dev, batch):
+    w = workloads.Workload(9, "bf16", 512, 300)
+    got, ref = _gateup_case(dev, w, 0, batch, out_dtype=torch.bfloat16)
+    assert_parity(got, ref["h"], h_tol(ref, bf16=True), f"bf16 out b{batch}")
+
+
+@pytest.mark.parametrize("batch", [1, 2, 16, 32])
+def test_up_scale_doubling_is_exact(dev, batch):
+    """Up scale bytes e -> e+1 doubles u exactly and leaves silu(g)
+    unchanged, so h doubles bit for bit (on the device alone)."""
+    w = workloads.Workload(9, "dbl", 1024, 200)
+    g, u = workloads.gateup(w)
+    x = workloads.activations(w.wid, 0, batch, w.hidden)
+    xd = dev_bf16(x, dev)
+    p1 = dev_u8(tt.pack_mxfp4_gateup(g, u, w.inter, w.hidden), dev)
+    p2 = dev_u8(tt.pack_mxfp4_gateup(g, (u[0], u[1] + 1, u[2]), w.inter, w.hidden), dev)
+    h1 = tt.mxfp4_gateup_swiglu(p1, w.inter, w.hidden, xd)
+    h2 = tt.mxfp4_gateup_swiglu(p2, w.inter, w.hidden, xd)
+    assert torch.equal(h2, 2 * h1)
+
+
+@pytest.mark.parametrize("batch", [1, 8])
+def test_run_to_run_bit_identical(dev, batch):
+    w = workloads.SMOLLM3
+    g, u = workloads.gateup(w, 3)
+    x = dev_bf16(workloads.activations(w.wid, 3, batch, w.hidden), dev)
+    packed = dev_u8(tt.pack_mxfp4_gateup(g, u, w.inter, w.hidden), dev)
+    a = tt.mxfp4_gateup_swiglu(packed, w.inter, w.hidden, x)
+    b = tt.mxfp4_gateup_swiglu(packed, w.inter, w.hidden, x)
+    assert torch.equal(a, b)
+
+
+def test_one_hot_up_column_gives_silu_of_gate(dev):
+    """Up column j is code 2 (1.0) under scale 127 with postscale 1 and every
+    other up code 0; x = e_j makes u = 1 exactly, so h = silu(ps_g w_g[:, j])."""
+    w = workloads.Workload(9, "onehot", 256, 64)
+    g, _ = workloads.gateup(w)
+    j = 77
+    uc = np.zeros((w.inter, w.hidden // 2), np.uint8)
+    uc[:, j // 2] = 2 << 4 if j & 1 else 2
+    us = np.full((w.inter, w.hidden // 32), 127, np.uint8)
+    u = (uc, us, np.ones(w.inter, np.float32))
+    x = np.zeros((1, w.hidden), np.uint16)
+    x[0, j] = 0x3F80
+    got, ref = _gateup_case(dev, w, 0, 1, g=g, u=u, x=x)
+    assert np.all(ref["u"] == 1.0)
+    assert_parity(got, ref["h"], 4e-7 * np.abs(ref["h"]) + 1e-30, "one-hot up column")
