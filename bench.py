@@ -69,6 +69,7 @@ def setup_gateup(tt, torch, dev, w, layers, batch, distinct=None):
 
 
 def time_steps(torch, step, steps, warmup):
+    """Eager timing: `steps` back-to-back steps between two events."""
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -80,6 +81,25 @@ def time_steps(torch, step, steps, warmup):
     stop.record()
     torch.cuda.synchronize()
     return start.elapsed_time(stop) / 1e3  # seconds
+
+
+def capture(torch, step):
+    """One step captured as a HIP graph (the decode loop's launch path)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, graph, steps, warmup):
+    return time_steps(torch, graph.replay, steps, warmup)
 
 
 def cpu_baseline_gateup(w, seconds):
@@ -130,7 +150,8 @@ def run(args):
             for i in range(layers):
                 tt.mxfp4_gateup_swiglu(packs[i], w.inter, w.hidden, xs[i], out=outs[i])
 
-        secs = time_steps(torch, step, K, W)
+        eager = time_steps(torch, step, K, W)
+        secs = time_graph(torch, capture(torch, step), K, W)
         calls = K * layers
         per_call = gateup_bytes(w.inter, w.hidden, batch)
         us_call = secs / calls * 1e6
@@ -139,9 +160,11 @@ def run(args):
         result = dict(metric="effective HBM GB/s of the MXFP4 gate/up SwiGLU GEMV "
                              "(us/call alongside)",
                       value=round(gbs, 2), unit="GB/s", us_per_call=round(us_call, 3),
+                      us_per_call_eager=round(eager / calls * 1e6, 3),
                       ms_per_step=round(secs / K * 1e3, 4), bytes_per_call=per_call,
                       config=dict(workload=w.name, hidden=w.hidden, inter=w.inter, batch=batch,
-                                  layers_rotated=layers, calls_per_step=layers),
+                                  layers_rotated=layers, calls_per_step=layers,
+                                  launch="one HIP graph per step"),
                       roofline=dict(bound="hbm", kernel=kernel, achieved=round(gbs, 2),
                                     peak=PEAK_HBM_GBS, unit="GB/s",
                                     frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
@@ -173,7 +196,7 @@ def run(args):
                 tt.int4_gemv(pq, nq, kq, x, out=yq)
                 tt.int4_gemv(po, no, ko, x, out=yo)
 
-        secs = time_steps(torch, step, K, W)
+        secs = time_graph(torch, capture(torch, step), K, W)
         per_pair = int4_bytes(nq, kq, 1) + int4_bytes(no, ko, 1)
         calls = K * copies * 2
         gbs = per_pair * copies * K / secs / 1e9
@@ -181,7 +204,8 @@ def run(args):
                       value=round(gbs, 2), unit="GB/s", us_per_call=round(secs / calls * 1e6, 3),
                       ms_per_step=round(secs / K * 1e3, 4),
                       config=dict(workload="phi4-14b-int4-qkv-o", qkv=[nq, kq], o=[no, ko],
-                                  group=128, copies_rotated=copies),
+                                  group=128, copies_rotated=copies,
+                                  launch="one HIP graph per step"),
                       roofline=dict(bound="hbm", kernel="k_int4_gemv", achieved=round(gbs, 2),
                                     peak=PEAK_HBM_GBS, unit="GB/s",
                                     frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
@@ -206,24 +230,20 @@ def run(args):
         gu0 = torch.from_numpy(gu).to(dev)
         dn0 = torch.from_numpy(dn).to(dev)
         banks = [(gu0, dn0)] + [(gu0.clone(), dn0.clone()) for _ in range(layers - 1)]
-        nlog = 64
         logits = [torch.from_numpy(workloads.router_logits(w.wid, s, 1, E).view(np.int16)).to(dev)
-                  for s in range(nlog)]
+                  for s in range(layers)]
         x = torch.from_numpy(workloads.activations(w.wid, 0, 1, w.hidden).view(np.int16)).to(dev)
         ids = torch.empty((1, w.topk), dtype=torch.int32, device=dev)
         wt = torch.empty((1, w.topk), dtype=torch.float32, device=dev)
         h = torch.empty((1, w.topk, w.inter), dtype=torch.bfloat16, device=dev)
         y = torch.empty((1, w.hidden), dtype=torch.float32, device=dev)
-        state = {"i": 0}
-
         def step():
             for li, (g_, d_) in enumerate(banks):
-                tt.moe_route_topk(logits[(state["i"] + li) % nlog], w.topk, ids=ids, w=wt)
+                tt.moe_route_topk(logits[li], w.topk, ids=ids, w=wt)
                 tt.moe_mxfp4_gateup_swiglu(g_, E, w.inter, w.hidden, x, ids, out=h)
                 tt.moe_mxfp4_down_combine(d_, E, w.hidden, w.inter, h, ids, wt, out=y)
-            state["i"] += 1
 
-        secs = time_steps(torch, step, K, W)
+        secs = time_graph(torch, capture(torch, step), K, W)
         per_layer = (w.topk * (2 * mx_matrix_bytes(w.inter, w.hidden)) + w.hidden * 2
                      + w.topk * w.inter * 2) + (w.topk * mx_matrix_bytes(w.hidden, w.inter)
                                                 + w.topk * w.inter * 2 + w.hidden * 4)
@@ -234,7 +254,9 @@ def run(args):
                       us_per_layer=round(secs / (K * layers) * 1e6, 3),
                       ms_per_step=round(secs / K * 1e3, 4),
                       config=dict(workload=w.name, hidden=w.hidden, inter=w.inter, experts=E,
-                                  topk=w.topk, batch=1, layers_rotated=layers, h_dtype="bf16"),
+                                  topk=w.topk, batch=1, layers_rotated=layers, h_dtype="bf16",
+                                  routing="a distinct seeded routing per layer",
+                                  launch="one HIP graph per step"),
                       roofline=dict(bound="hbm", kernel="k_gateup_valu+k_down_combine",
                                     achieved=round(gbs, 2), peak=PEAK_HBM_GBS, unit="GB/s",
                                     frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
@@ -254,6 +276,20 @@ def run(args):
     print(json.dumps(out), flush=True)
 
 
+def copy_probe(mib, reps):
+    """A plain device-to-device copy of a known size (for normalising the
+    HBM byte counters of a profiler run against a known transfer)."""
+    import torch
+    dev = torch.device("cuda", 0)
+    n = mib << 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps(dict(probe="copy", bytes_read=n, bytes_written=n, reps=reps)), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -264,7 +300,12 @@ def main():
     ap.add_argument("--batch", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (profiler calibration)")
     args = ap.parse_args()
+    if args.copy_probe:
+        copy_probe(args.copy_probe, 4)
+        return
     if args.gpus != 1:
         print(f"bench.py measures a single GPU; --gpus {args.gpus} is not supported: the "
               "projections are measured on one MI355X only.", file=sys.stderr)

@@ -126,6 +126,12 @@ __global__ __launch_bounds__(1024) void k_down_combine(DownArgs a) {
     const bool valid = e >= 0 && e < a.n_experts;
     const int r = lane & 15, q = lane >> 4;
     float acc = 0.0f;
+    // postscale of this slot's expert for the tile's rows, fetched up front
+    float psj = 0.0f;
+    if (valid && part == 0 && lane < 16)
+        psj = reinterpret_cast<const float *>(a.bank + (int64_t)e * a.expert_stride +
+                                              (int64_t)tile * a.tile_stride + a.ps_off)[lane];
+    const float wj = a.wt[b * a.topk + j];
     if (valid) {
         const uint8_t *tb = a.bank + (int64_t)e * a.expert_stride + (int64_t)tile * a.tile_stride;
         const uint8_t *sp = tb + a.scale_off + lane * 4;
@@ -163,22 +169,19 @@ __global__ __launch_bounds__(1024) void k_down_combine(DownArgs a) {
     }
     acc += __shfl_xor(acc, 16);
     acc += __shfl_xor(acc, 32);
+    // per slot: 16 postscales, then its routing weight (NaN marks a bad id)
+    float *pss = red + a.topk * a.S * 16;
     if (lane < 16) red[wave * 16 + lane] = acc;
+    if (part == 0 && lane < 16) pss[j * 17 + lane] = psj;
+    if (part == 0 && lane == 16) pss[j * 17 + 16] = valid ? wj : __builtin_nanf("");
     __syncthreads();
     if (wave != 0 || lane >= 16) return;
     const int row = tile * 16 + lane;
     float y = 0.0f;
     for (int jj = 0; jj < a.topk; ++jj) {
-        const int ee = a.ids[b * a.topk + jj];
-        if (ee < 0 || ee >= a.n_experts) {
-            y = __builtin_nanf("");
-            continue;
-        }
         float dot = red[(jj * a.S) * 16 + lane];
         for (int pp = 1; pp < a.S; ++pp) dot += red[(jj * a.S + pp) * 16 + lane];
-        const float ps = reinterpret_cast<const float *>(
-            a.bank + (int64_t)ee * a.expert_stride + (int64_t)tile * a.tile_stride + a.ps_off)[lane];
-        y += a.wt[b * a.topk + jj] * (ps * dot);
+        y += pss[jj * 17 + 16] * (pss[jj * 17 + lane] * dot);
     }
     if (row < a.hidden) store_out(a.y, (int64_t)b * a.hidden + row, y, a.y_bf16);
 }
@@ -252,7 +255,8 @@ extern "C" tt_status tt_moe_mxfp4_down_combine(const void *down_bank, int64_t n_
     while (S > 1 && (int)ceil_div(g.units, S) < 4) S /= 2;
     a.S = S < 1 ? 1 : S;
     const size_t esz = h_dtype == TT_F32 ? 4 : 2;
-    const size_t lds = (size_t)topk * g.units * 128 * esz + (size_t)topk * a.S * 64;
+    const size_t lds = (size_t)topk * g.units * 128 * esz + (size_t)topk * a.S * 64 +
+                       (size_t)topk * 17 * 4;
     if (lds > 64 * 1024) {
         static bool raised[2][64] = {{false}};
         int dev = 0;

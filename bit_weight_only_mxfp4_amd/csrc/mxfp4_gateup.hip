@@ -158,6 +158,12 @@ __global__ __launch_bounds__(512) void k_gateup_valu(GateUpArgs a) {
         for (int i = 4 * g; i < 4 * g + 4; ++i)
             c[i] = load16(rs, i < n ? voff + i * kUnitBytes : kOob);
     }
+    // the row postscales (lanes 0..15 of the wave that finishes the tile) are
+    // fetched with the weights, not after the reduction, so the epilogue adds
+    // no dependent memory round trip
+    const float ps = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(
+                   rs, (part == 0 && lane < 16 && tile_ok) ? a.ps_off + lane * 4 : kOob, 0, 0));
 
     // 3. activations to LDS (zero past K), then an LDS-only barrier
 #pragma unroll
@@ -189,7 +195,6 @@ __global__ __launch_bounds__(512) void k_gateup_valu(GateUpArgs a) {
         }
     }
     if (!tile_ok) return;
-    const float ps = (lane < 16) ? reinterpret_cast<const float *>(tb + a.ps_off)[lane] : 0.0f;
     const float y = acc * ps;             // tile rows 0..7 gate, 8..15 up
     const float u = __shfl_down(y, 8);
     const int pair = tile * 8 + lane;
@@ -216,6 +221,8 @@ __global__ __launch_bounds__(512) void k_gateup_mfma(GateUpArgs a) {
     for (int tile = blockIdx.x * nw + wave; tile < a.ntiles; tile += gridDim.x * nw) {
         const uint8_t *tb = a.w + (int64_t)tile * a.tile_stride;
         const uint8_t *sp = tb + a.scale_off + lane * 4;
+        // lane (token column, row group q) needs the postscales of rows 4q..4q+3
+        const float4 ps4 = reinterpret_cast<const float4 *>(tb + a.ps_off)[q];
         f32x4_t C[NCOL];
 #pragma unroll
         for (int cb = 0; cb < NCOL; ++cb) C[cb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -253,7 +260,6 @@ __global__ __launch_bounds__(512) void k_gateup_mfma(GateUpArgs a) {
             }
         }
         // lane (token column r, row group q) holds rows 4q..4q+3 of the tile
-        const float4 ps4 = reinterpret_cast<const float4 *>(tb + a.ps_off)[q];
         const float psv[4] = {ps4.x, ps4.y, ps4.z, ps4.w};
 #pragma unroll
         for (int cb = 0; cb < NCOL; ++cb) {

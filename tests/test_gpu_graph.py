@@ -1,0 +1,83 @@
+"""The device calls under HIP graph capture: every replay must reproduce
+the eager result, with eager work and synchronisations between replays."""
+import numpy as np
+import pytest
+import torch
+
+import bit_weight_only_mxfp4_amd as tt
+import workloads
+from _parity import dev_bf16, dev_u8
+
+pytestmark = pytest.mark.gpu
+
+
+def _capture(fn):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def test_graph_replays_match_eager(dev):
+    w = workloads.Workload(9, "graph", 2880, 1024, n_experts=6, topk=4)
+    g, u = workloads.gateup(w)
+    gu = dev_u8(tt.pack_mxfp4_gateup(g, u, w.inter, w.hidden), dev)
+    gb = workloads.expert_bank(w, 0, "gate")
+    ub = workloads.expert_bank(w, 0, "up")
+    db = workloads.expert_bank(w, 0, "down")
+    gs = tt.mxfp4_gateup_pack_bytes(w.inter, w.hidden)
+    ds = tt.mxfp4_matrix_pack_bytes(w.hidden, w.inter)
+    bank = np.empty(6 * gs, np.uint8)
+    down = np.empty(6 * ds, np.uint8)
+    for e in range(6):
+        tt.pack_mxfp4_gateup((gb[0][e], gb[1][e], gb[2][e]), (ub[0][e], ub[1][e], ub[2][e]),
+                             w.inter, w.hidden, out=bank[e * gs:(e + 1) * gs])
+        tt.pack_mxfp4_matrix(db[0][e], db[1][e], db[2][e], w.hidden, w.inter,
+                             out=down[e * ds:(e + 1) * ds])
+    bank, down = dev_u8(bank, dev), dev_u8(down, dev)
+    wq = workloads.int4_source(2, 0, 384, w.hidden)
+    q4 = dev_u8(tt.pack_int4(*tt.quantize_int4_affine(wq), 384, w.hidden), dev)
+
+    x1 = dev_bf16(workloads.activations(9, 0, 1, w.hidden), dev)
+    x8 = dev_bf16(workloads.activations(9, 1, 8, w.hidden), dev)
+    lg = dev_bf16(workloads.router_logits(9, 0, 1, 6), dev)
+    outs = dict(h1=torch.empty((1, w.inter), device=dev), h8=torch.empty((8, w.inter), device=dev),
+                ids=torch.empty((1, 4), dtype=torch.int32, device=dev),
+                wt=torch.empty((1, 4), device=dev),
+                he=torch.empty((1, 4, w.inter), dtype=torch.bfloat16, device=dev),
+                y=torch.empty((1, w.hidden), device=dev), q=torch.empty((1, 384), device=dev))
+
+    def step():
+        tt.mxfp4_gateup_swiglu(gu, w.inter, w.hidden, x1, out=outs["h1"])
+        tt.mxfp4_gateup_swiglu(gu, w.inter, w.hidden, x8, out=outs["h8"])
+        tt.moe_route_topk(lg, 4, ids=outs["ids"], w=outs["wt"])
+        tt.moe_mxfp4_gateup_swiglu(bank, 6, w.inter, w.hidden, x1, outs["ids"], out=outs["he"])
+        tt.moe_mxfp4_down_combine(down, 6, w.hidden, w.inter, outs["he"], outs["ids"],
+                                  outs["wt"], out=outs["y"])
+        tt.int4_gemv(q4, 384, w.hidden, x1, out=outs["q"])
+
+    graph = _capture(step)
+    gen = np.random.default_rng(0)
+    for rep in range(4):
+        # new inputs in place (eager work between replays)
+        x1.copy_(dev_bf16(workloads.bf16_bits(gen.standard_normal((1, w.hidden))
+                                              .astype(np.float32)), dev))
+        lg.copy_(dev_bf16(workloads.bf16_bits(gen.standard_normal((1, 6))
+                                              .astype(np.float32)), dev))
+        torch.cuda.synchronize()
+        step()
+        torch.cuda.synchronize()
+        eager = {k: v.clone() for k, v in outs.items()}
+        for v in outs.values():
+            v.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in outs:
+            assert torch.equal(outs[k], eager[k]), (rep, k)
