@@ -68,6 +68,25 @@ def setup_gateup(tt, torch, dev, w, layers, batch, distinct=None):
     return packs, xs
 
 
+def profiled_traffic(kernel_sources, summary):
+    """HBM bytes per launch recorded in a profiles/ summary, or None when the
+    kernel's sources have changed since those counters were taken."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in kernel_sources:
+        with open(os.path.join(ROOT, "bit_weight_only_mxfp4_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    try:
+        with open(os.path.join(ROOT, "profiles", summary)) as fh:
+            fields = dict(ln.split(":", 1) for ln in fh if ln.startswith(("source_sha256:",
+                                                                       "traffic_bytes_per_launch:")))
+    except OSError:
+        return None
+    if fields.get("source_sha256", "").strip() != h.hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def time_steps(torch, step, steps, warmup):
     """Eager timing: `steps` back-to-back steps between two events."""
     for _ in range(warmup):
@@ -168,6 +187,9 @@ def run(args):
                       roofline=dict(bound="hbm", kernel=kernel, achieved=round(gbs, 2),
                                     peak=PEAK_HBM_GBS, unit="GB/s",
                                     frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
+        if args.workload == "smollm3":
+            result["roofline"]["traffic"] = profiled_traffic(
+                ("mxfp4_gateup.hip", "device.h", "layout.h"), "gateup_smollm3_b1.md")
         if not args.no_cpu_baseline and args.workload in ("smollm3", "tiny"):
             log("cpu baseline (oracle) ...")
             result["cpu_baseline"] = cpu_baseline_gateup(w, args.cpu_seconds)
