@@ -15,7 +15,7 @@ with us_per_call, the roofline of the kernel and the CPU oracle timed on the
 host (a reported baseline, not a target).
 
 Other workloads (--workload): tiny, phi4 (gate/up), phi4-int4 (QKV + O),
-gptoss (route + expert gate/up + down), batched (--batch B).
+gptoss (route + expert gate/up + down/combine), batched (--batch B).
 """
 from __future__ import annotations
 
@@ -271,7 +271,7 @@ def run(args):
                                                 + w.topk * w.inter * 2 + w.hidden * 4)
         gbs = per_layer * layers * K / secs / 1e9
         result = dict(metric="effective HBM GB/s of the routed-expert MXFP4 layer "
-                             "(route + gate/up SwiGLU + down/combine)",
+                             "(route + expert gate/up SwiGLU + down/combine)",
                       value=round(gbs, 2), unit="GB/s",
                       us_per_layer=round(secs / (K * layers) * 1e6, 3),
                       ms_per_step=round(secs / K * 1e3, 4),
@@ -279,7 +279,7 @@ def run(args):
                                   topk=w.topk, batch=1, layers_rotated=layers, h_dtype="bf16",
                                   routing="a distinct seeded routing per layer",
                                   launch="one HIP graph per step"),
-                      roofline=dict(bound="hbm", kernel="k_gateup_valu+k_down_combine",
+                      roofline=dict(bound="hbm", kernel="k_route_topk+k_gateup_valu+k_down_combine",
                                     achieved=round(gbs, 2), peak=PEAK_HBM_GBS, unit="GB/s",
                                     frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
     else:

@@ -47,6 +47,8 @@ _SIGS = {
     "tt_moe_route_topk": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "tt_moe_mxfp4_gateup_swiglu": (_I32, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P,
                                           _I32, _P]),
+    "tt_moe_mxfp4_route_gateup_swiglu": (_I32, [_P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P,
+                                                _P, _P, _I32, _P]),
     "tt_moe_mxfp4_down_combine": (_I32, [_P, _I64, _I64, _I64, _P, _I32, _P, _P, _I64,
                                          _I64, _P, _I32, _P]),
     "tt_int4_gemv": (_I32, [_P, _I64, _I64, _I64, _P, _I64, _P, _I32, _P]),
@@ -243,6 +245,28 @@ def moe_mxfp4_gateup_swiglu(bank, n_experts, inter, hidden, x, ids, out=None, ou
                                           _dev_ptr(out, "h"), _dtype_code(out.dtype),
                                           _stream(x)))
     return out
+
+
+def moe_mxfp4_route_gateup_swiglu(bank, n_experts, inter, hidden, x, logits, topk, ids=None,
+                                  w=None, out=None, out_dtype=None):
+    """Routing fused into the expert gate/up; returns (h, ids, w)."""
+    torch = _torch()
+    _acts(x)
+    _acts(logits, "logits")
+    batch = x.numel() // hidden
+    if ids is None:
+        ids = torch.empty((batch, topk), dtype=torch.int32, device=x.device)
+    if w is None:
+        w = torch.empty((batch, topk), dtype=torch.float32, device=x.device)
+    if out is None:
+        out = torch.empty((batch, topk, inter), dtype=out_dtype or torch.float32,
+                          device=x.device)
+    _check(lib.tt_moe_mxfp4_route_gateup_swiglu(
+        _dev_ptr(bank, "bank", (torch.uint8,)), n_experts, inter, hidden, _dev_ptr(x, "x"), batch,
+        _dev_ptr(logits, "logits"), topk, _dev_ptr(ids, "ids", (torch.int32,)),
+        _dev_ptr(w, "w", (torch.float32,)), _dev_ptr(out, "h"), _dtype_code(out.dtype),
+        _stream(x)))
+    return out, ids, w
 
 
 def moe_mxfp4_down_combine(down_bank, n_experts, hidden, inter, h, ids, w, out=None,

@@ -3,9 +3,10 @@
 // "Implemented a huge list of fixes": affine INT4 with a partial last group):
 //   y[b][r] = sum_g s[r][g] * sum_{k in g} (q[r][k] - z[r][g]) * x[b][k]
 //
-// Layout and grid follow the MXFP4 kernel: one workgroup per 16-row tile, KS
+// Layout and grid follow the MXFP4 kernel: one workgroup per 16-row tile, ks
 // waves splitting the groups, one 16-byte load per lane per unit (32 codes of
-// one row; a unit is one 128-element group).  Decode: a code q becomes the
+// one row; a unit is one 128-element group), all of a wave's loads in flight
+// before the activations are staged.  Decode: a code q becomes the
 // bf16 number 128 + q by OR-ing it under the exponent pattern 0x4300 (exact),
 // two at a time, and a dot2 accumulates (128 + q) * x in fp32.  Per 32-element
 // piece the activations' plain sum X is staged once, so the group term is
@@ -26,9 +27,15 @@ struct I4Args {
     int32_t batch;
     void *y;            // [batch][n]
     int32_t y_bf16;
+    int32_t ks;         // waves per tile
+    int32_t xvec;       // x rows are 16-byte aligned (k % 8 == 0 and x aligned)
 };
 
-constexpr int kI4PF = 8;
+// Tuning: units (128-element groups) per wave; a tile uses at most 16 waves.
+#ifndef TT_INT4_UPW
+#define TT_INT4_UPW 4
+#endif
+constexpr int kOob = 0x7FFFFF00;  // buffer offset past every tile: loads return 0
 
 // (128 + q) x summed over the 8 codes of one dword; xg holds the reordered
 // activation pairs of that 8-element group.
@@ -44,80 +51,132 @@ __device__ __forceinline__ float i4x8_dot(uint32_t c, uint4 xg, float acc) {
     return acc;
 }
 
-template <int KS, int NT>
-__global__ __launch_bounds__(64 * KS) void k_int4_gemv(I4Args a) {
+__device__ __forceinline__ uint4 i4_load16(__amdgpu_buffer_rsrc_t r, int off) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void i4_lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// One workgroup per 16-row tile and NT tokens; wave p owns units
+// [p * UPW, p * UPW + UPW).  Issue order per wave: the activations of its
+// pieces, then each s|z group followed by its four code units.  Units past K
+// read at an out-of-range buffer offset (zeros) and meet zero-padded
+// activations and zero piece sums, so they add exactly nothing.
+template <int UPW, int NT>
+__global__ __launch_bounds__(1024) void k_int4_gemv(I4Args a) {
+    static_assert(UPW % 4 == 0 && UPW <= 16, "units per wave");
     extern __shared__ __align__(16) uint8_t smem[];
-    const int kp = a.units * 128;  // padded K
-    uint16_t *xs = reinterpret_cast<uint16_t *>(smem);                       // [NT][kp]
-    float *xsum = reinterpret_cast<float *>(smem + (size_t)NT * kp * 2);     // [NT][kp/32]
-    float *red = xsum + NT * (kp / 32);                                      // [KS][NT][16]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ks = a.ks;
+    const int kp = ks * UPW * 128;   // staged K per token, zero past a.k
+    const int pieces = kp / 32;      // <= nthreads (UPW <= 16)
+    uint16_t *xs = reinterpret_cast<uint16_t *>(smem);                   // [NT][kp]
+    float *xsum = reinterpret_cast<float *>(smem + (size_t)NT * kp * 2); // [NT][pieces]
+    float *red = xsum + NT * pieces;                                     // [ks][NT][16]
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tile = blockIdx.x, t0 = blockIdx.y * NT;
     const int nt = min(NT, a.batch - t0);
 
-    // stage: one thread per (token, 32-element piece)
-    const int pieces = kp / 32;
-    for (int i = tid; i < NT * pieces; i += 64 * KS) {
-        const int t = i / pieces, p = i % pieces;
-        uint4 *dst = reinterpret_cast<uint4 *>(xs + t * kp + p * 32);
-        float sum = 0.0f;
-        const uint16_t *src = a.x + (int64_t)(t0 + t) * a.k;
+    // 1. activations: thread tid fetches piece tid of every token
+    uint32_t xw[NT][16];
+    const bool xvec = a.xvec != 0;
+    {
+        const int p = tid;
 #pragma unroll
-        for (int g8 = 0; g8 < 4; ++g8) {
-            uint32_t v[8];
+        for (int t = 0; t < NT; ++t) {
+            const uint16_t *src = a.x + (int64_t)(t0 + t) * a.k + p * 32;
+            const bool tok_ok = t < nt;
+            if (xvec) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int kk = p * 32 + g8 * 8 + j;
-                v[j] = (t < nt && kk < a.k) ? src[kk] : 0u;
-                sum += bf16_bits_to_f32(v[j]);
+                for (int g8 = 0; g8 < 4; ++g8) {
+                    const bool ok = tok_ok && p * 32 + g8 * 8 < a.k;
+                    const uint4 v = ok ? reinterpret_cast<const uint4 *>(src)[g8]
+                                       : make_uint4(0, 0, 0, 0);
+                    xw[t][4 * g8 + 0] = v.x;
+                    xw[t][4 * g8 + 1] = v.y;
+                    xw[t][4 * g8 + 2] = v.z;
+                    xw[t][4 * g8 + 3] = v.w;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int k0 = p * 32 + 2 * j;
+                    const uint32_t lo = (tok_ok && k0 < a.k) ? src[2 * j] : 0u;
+                    const uint32_t hi = (tok_ok && k0 + 1 < a.k) ? src[2 * j + 1] : 0u;
+                    xw[t][j] = lo | (hi << 16);
+                }
             }
-            dst[g8] = make_uint4(v[0] | (v[4] << 16), v[1] | (v[5] << 16), v[2] | (v[6] << 16),
-                                 v[3] | (v[7] << 16));
         }
-        xsum[t * pieces + p] = sum;
     }
-    __syncthreads();
 
+    // 2. weights
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(a.w + (int64_t)tile * a.tile_stride), 0, (int)a.tile_stride,
+        0x00020000);
     const int r = lane & 15, q = lane >> 4;
-    const uint8_t *tb = a.w + (int64_t)tile * a.tile_stride;
-    const int upw = (a.units + KS - 1) / KS;
-    const int u0 = wave * upw, u1 = min(a.units, u0 + upw);
+    const int u0 = wave * UPW;
+    const int n = max(0, min(UPW, a.units - u0));
+    uint4 c[UPW];
+    uint4 szv[UPW / 4];
+    const int voff = u0 * kUnitBytes + lane * 16;
+    const int soff = a.sz_off + (u0 >> 2) * kGroupBytes + r * 16;
+#pragma unroll
+    for (int g = 0; g < UPW / 4; ++g) {
+        szv[g] = i4_load16(rs, 4 * g < n ? soff + g * kGroupBytes : kOob);
+#pragma unroll
+        for (int i = 4 * g; i < 4 * g + 4; ++i)
+            c[i] = i4_load16(rs, i < n ? voff + i * kUnitBytes : kOob);
+    }
+
+    // 3. activations to LDS: 8-element groups reordered as (x0,x4) (x1,x5)
+    //    (x2,x6) (x3,x7), plus the plain sum of each 32-element piece
+    if (tid < pieces) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            uint4 *dst = reinterpret_cast<uint4 *>(xs + t * kp + tid * 32);
+            float sum = 0.0f;
+#pragma unroll
+            for (int g8 = 0; g8 < 4; ++g8) {
+                const uint32_t w0 = xw[t][4 * g8], w1 = xw[t][4 * g8 + 1];
+                const uint32_t w2 = xw[t][4 * g8 + 2], w3 = xw[t][4 * g8 + 3];
+                // elements e0..e7 = lo(w0) hi(w0) lo(w1) hi(w1) lo(w2) hi(w2) lo(w3) hi(w3)
+                dst[g8] = make_uint4((w0 & 0xFFFFu) | (w2 << 16), (w0 >> 16) | (w2 & 0xFFFF0000u),
+                                     (w1 & 0xFFFFu) | (w3 << 16), (w1 >> 16) | (w3 & 0xFFFF0000u));
+                sum += bf16_bits_to_f32(w0 & 0xFFFFu) + bf16_bits_to_f32(w0 >> 16) +
+                       bf16_bits_to_f32(w1 & 0xFFFFu) + bf16_bits_to_f32(w1 >> 16) +
+                       bf16_bits_to_f32(w2 & 0xFFFFu) + bf16_bits_to_f32(w2 >> 16) +
+                       bf16_bits_to_f32(w3 & 0xFFFFu) + bf16_bits_to_f32(w3 >> 16);
+            }
+            xsum[t * pieces + tid] = sum;
+        }
+    }
+    i4_lds_barrier();
+
+    // 4. consume the units in load order
     float acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = 0.0f;
-    for (int kb = u0; kb < u1; kb += kI4PF) {
-        uint4 c[kI4PF];
-        uint32_t sz[kI4PF];
 #pragma unroll
-        for (int i = 0; i < kI4PF; ++i) {
-            const int kk = kb + i;
-            if (kk < u1) {
-                const int off = kk * kUnitBytes +
-                                ((kk == a.units - 1 && q >= a.qv_last) ? r * 16 : lane * 16);
-                c[i] = *reinterpret_cast<const uint4 *>(tb + off);
-                sz[i] = *reinterpret_cast<const uint32_t *>(tb + a.sz_off + (kk >> 2) * kGroupBytes +
-                                                            r * 16 + (kk & 3) * 4);
-            }
-        }
+    for (int i = 0; i < UPW; ++i) {
+        const uint32_t sz = (i & 3) == 0 ? szv[i >> 2].x
+                          : (i & 3) == 1 ? szv[i >> 2].y
+                          : (i & 3) == 2 ? szv[i >> 2].z : szv[i >> 2].w;
+        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(sz & 0xFFFFu));
+        const float zb = 128.0f + (float)__builtin_bit_cast(_Float16, (uint16_t)(sz >> 16));
+        const int p = 4 * (u0 + i) + q;
 #pragma unroll
-        for (int i = 0; i < kI4PF; ++i) {
-            const int kk = kb + i;
-            if (kk < u1) {
-                const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(sz[i] & 0xFFFFu));
-                const float zb = 128.0f + (float)__builtin_bit_cast(_Float16, (uint16_t)(sz[i] >> 16));
-                const int p = 4 * kk + q;
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    if (t < nt) {
-                        const uint4 *xg = reinterpret_cast<const uint4 *>(xs + t * kp + p * 32);
-                        float d0 = i4x8_dot(c[i].x, xg[0], 0.0f);
-                        float d1 = i4x8_dot(c[i].y, xg[1], 0.0f);
-                        d0 = i4x8_dot(c[i].z, xg[2], d0);
-                        d1 = i4x8_dot(c[i].w, xg[3], d1);
-                        acc[t] = fmaf(s, fmaf(-zb, xsum[t * pieces + p], d0 + d1), acc[t]);
-                    }
-                }
-            }
+        for (int t = 0; t < NT; ++t) {
+            const uint4 *xg = reinterpret_cast<const uint4 *>(xs + t * kp + p * 32);
+            float d0 = i4x8_dot(c[i].x, xg[0], 0.0f);
+            float d1 = i4x8_dot(c[i].y, xg[1], 0.0f);
+            d0 = i4x8_dot(c[i].z, xg[2], d0);
+            d1 = i4x8_dot(c[i].w, xg[3], d1);
+            acc[t] = fmaf(s, fmaf(-zb, xsum[t * pieces + p], d0 + d1), acc[t]);
         }
     }
 #pragma unroll
@@ -125,18 +184,17 @@ __global__ __launch_bounds__(64 * KS) void k_int4_gemv(I4Args a) {
         acc[t] += __shfl_xor(acc[t], 16);
         acc[t] += __shfl_xor(acc[t], 32);
     }
-    if (KS > 1) {
+    if (ks > 1) {
         if (lane < 16)
 #pragma unroll
             for (int t = 0; t < NT; ++t) red[(wave * NT + t) * 16 + lane] = acc[t];
-        __syncthreads();
+        i4_lds_barrier();
         if (wave != 0) return;
         if (lane < 16)
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 float v = red[t * 16 + lane];
-#pragma unroll
-                for (int w = 1; w < KS; ++w) v += red[(w * NT + t) * 16 + lane];
+                for (int w = 1; w < ks; ++w) v += red[(w * NT + t) * 16 + lane];
                 acc[t] = v;
             }
     }
@@ -149,30 +207,32 @@ __global__ __launch_bounds__(64 * KS) void k_int4_gemv(I4Args a) {
 
 namespace {
 
-int pick_ks(int units) {
-    if (units >= 48) return 8;
-    if (units >= 24) return 4;
-    if (units >= 12) return 2;
-    return 1;
-}
-
 constexpr size_t kLdsBudget = 64 * 1024;
 
-size_t lds_bytes(int units, int nt, int ks) {
-    const size_t kp = (size_t)units * 128;
+size_t lds_bytes(int ks, int upw, int nt) {
+    const size_t kp = (size_t)ks * upw * 128;
     return (size_t)nt * kp * 2 + (size_t)nt * (kp / 32) * 4 + (size_t)ks * nt * 64;
 }
 
-template <int NT>
-tt_status launch_nt(const I4Args &a, int ks, hipStream_t s) {
-    const size_t lds = lds_bytes(a.units, NT, ks);
+template <int UPW, int NT>
+tt_status launch_i4(I4Args a, hipStream_t s) {
+    a.ks = (int32_t)ceil_div(a.units, UPW);
     dim3 grid(a.ntiles, (a.batch + NT - 1) / NT);
-    const char *what = "int4 gemv";
-    switch (ks) {
-        case 1: return launch(what, k_int4_gemv<1, NT>, grid, dim3(64), lds, s, a);
-        case 2: return launch(what, k_int4_gemv<2, NT>, grid, dim3(128), lds, s, a);
-        case 4: return launch(what, k_int4_gemv<4, NT>, grid, dim3(256), lds, s, a);
-        default: return launch(what, k_int4_gemv<8, NT>, grid, dim3(512), lds, s, a);
+    return launch("int4 gemv", k_int4_gemv<UPW, NT>, grid, dim3(64 * a.ks),
+                  lds_bytes(a.ks, UPW, NT), s, a);
+}
+
+template <int UPW>
+tt_status launch_upw(const I4Args &a, hipStream_t s) {
+    // tokens per weight pass: as many as the batch needs, as LDS allows
+    const int ks = (int)ceil_div(a.units, UPW);
+    int nt = a.batch == 1 ? 1 : a.batch == 2 ? 2 : a.batch <= 4 ? 4 : 8;
+    while (nt > 1 && lds_bytes(ks, UPW, nt) > kLdsBudget) nt /= 2;
+    switch (nt) {
+        case 1: return launch_i4<UPW, 1>(a, s);
+        case 2: return launch_i4<UPW, 2>(a, s);
+        case 4: return launch_i4<UPW, 4>(a, s);
+        default: return launch_i4<UPW, 8>(a, s);
     }
 }
 
@@ -212,20 +272,18 @@ extern "C" tt_status tt_int4_gemv(const void *w_packed, int64_t n, int64_t k, in
     a.batch = (int32_t)batch;
     a.y = y;
     a.y_bf16 = y_dtype == TT_BF16;
-    const int ks = pick_ks(a.units);
+    a.xvec = (k % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // tokens per weight pass: as many as the batch needs, as LDS allows
-    int nt = batch == 1 ? 1 : batch == 2 ? 2 : batch <= 4 ? 4 : 8;
-    while (nt > 1 && lds_bytes(a.units, nt, ks) > kLdsBudget) nt /= 2;
+    int upw = TT_INT4_UPW;
+    while (ceil_div(a.units, upw) > 16) upw += 4;
     tt_status st;
-    if (nt == 1)
-        st = launch_nt<1>(a, ks, s);
-    else if (nt == 2)
-        st = launch_nt<2>(a, ks, s);
-    else if (nt == 4)
-        st = launch_nt<4>(a, ks, s);
-    else
-        st = launch_nt<8>(a, ks, s);
+    switch (upw) {
+        case 4: st = launch_upw<4>(a, s); break;
+        case 8: st = launch_upw<8>(a, s); break;
+        case 12: st = launch_upw<12>(a, s); break;
+        case 16: st = launch_upw<16>(a, s); break;
+        default: return fail(TT_E_SHAPE, "k = %lld needs more than 8 waves per tile", (long long)k);
+    }
     if (st == TT_OK) clear_error();
     return st;
 }

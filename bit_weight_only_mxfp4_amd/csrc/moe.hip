@@ -3,9 +3,10 @@
 // Improvements": exact routing; "numerical drift & speedups": selected-expert
 // MXFP4 matvecs; "Dev Log #2": router and expert stages of an MoE model).
 //
-// Routing: one wave per token.  Each lane holds up to 4 bf16 logits; topk
-// rounds of a wave-wide (value, lower-index) maximum pick the experts in
-// descending order, and the weights are the softmax of the selected logits.
+// Routing: one wave per token.  Each expert's (bf16 logit, index) becomes one
+// orderable key; an expert's rank is the number of larger keys, and ranks
+// below topk are the selection in descending order, ties to the lower index.
+// The weights are the softmax of the selected logits.
 // Ids and weights stay on the device for the expert kernels.
 //
 // Down + combine: one workgroup per (16-row tile of the output, token) with
@@ -13,6 +14,8 @@
 // share of the K units against h[b][j] staged in LDS.  The per-row partials
 // are combined in a fixed order (parts, then slots j = 0..topk-1), so there
 // are no atomics and the result is bit-reproducible.
+#include <algorithm>
+
 #include "device.h"
 #include "tt_internal.h"
 
@@ -25,55 +28,59 @@ struct RouteArgs {
     float *w;
 };
 
+// Orderable 32-bit key of (bf16 logit, expert index): a larger key is a larger
+// logit, and among equal logits the lower index.  -0 is folded onto +0 so the
+// two compare equal, as the values do.
+__device__ __forceinline__ uint32_t route_key(uint32_t bits, int e) {
+    bits = (bits == 0x8000u) ? 0u : bits;
+    const uint32_t ord = (bits & 0x8000u) ? (~bits & 0xFFFFu) : (bits | 0x8000u);
+    return (ord << 16) | (0xFFFFu - (uint32_t)e);
+}
+
+// One wave per token.  Every lane writes the keys of its (up to 4) experts to
+// LDS, then counts how many keys exceed each of its own: that count is the
+// expert's rank, and ranks 0 .. topk-1 are the selection in descending order.
+// The selected lanes publish their logits by rank; lane 0 forms the softmax
+// over them in rank order.
 __global__ __launch_bounds__(64) void k_route_topk(RouteArgs ra) {
-    const uint16_t *logits = ra.logits;
+    __shared__ uint32_t keys[TT_MAX_EXPERTS];
+    __shared__ float selv[TT_MAX_TOPK];
+    __shared__ int32_t seli[TT_MAX_TOPK];
     const int n_exp = ra.n_exp, topk = ra.topk;
-    int32_t *ids = ra.ids;
-    float *w = ra.w;
     const int b = blockIdx.x, lane = threadIdx.x;
-    const uint16_t *lb = logits + (int64_t)b * n_exp;
-    float v[4];
-    bool live[4];
+    const uint16_t *lb = ra.logits + (int64_t)b * n_exp;
+    uint32_t raw[4], key[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw[i] = lb[min(lane + 64 * i, n_exp - 1)];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = lane + 64 * i;
-        live[i] = e < n_exp;
-        v[i] = live[i] ? bf16_bits_to_f32(lb[e]) : 0.0f;
+        key[i] = route_key(raw[i], e);
+        if (e < n_exp) keys[e] = key[i];
     }
-    float sel[TT_MAX_TOPK];
-    int sid[TT_MAX_TOPK];
-    for (int j = 0; j < topk; ++j) {
-        // best live candidate of this lane (its indices ascend with i)
-        float bv = 0.0f;
-        int bi = -1;
+    __syncthreads();
+    int rank[4] = {0, 0, 0, 0};
+    for (int e = 0; e < n_exp; ++e) {
+        const uint32_t k = keys[e];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (live[i] && (bi < 0 || v[i] > bv)) {
-                bv = v[i];
-                bi = lane + 64 * i;
-            }
-        // wave maximum, ties to the lower index; lanes without a candidate lose
+        for (int i = 0; i < 4; ++i) rank[i] += k > key[i] ? 1 : 0;
+    }
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off);
-            const int oi = __shfl_xor(bi, off);
-            const bool take = oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi));
-            bv = take ? ov : bv;
-            bi = take ? oi : bi;
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        if (e < n_exp && rank[i] < topk) {
+            selv[rank[i]] = bf16_bits_to_f32(raw[i]);
+            seli[rank[i]] = e;
         }
-        sel[j] = bv;
-        sid[j] = bi;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (lane + 64 * i == bi) live[i] = false;
     }
+    __syncthreads();
     if (lane == 0) {
-        const float m = sel[0];
+        const float m = selv[0];
         float den = 0.0f;
-        for (int j = 0; j < topk; ++j) den += expf(sel[j] - m);
+        for (int j = 0; j < topk; ++j) den += expf(selv[j] - m);
         for (int j = 0; j < topk; ++j) {
-            ids[(int64_t)b * topk + j] = sid[j];
-            w[(int64_t)b * topk + j] = expf(sel[j] - m) / den;
+            ra.ids[(int64_t)b * topk + j] = seli[j];
+            ra.w[(int64_t)b * topk + j] = expf(selv[j] - m) / den;
         }
     }
 }
@@ -86,106 +93,166 @@ struct DownArgs {
     const void *h;                     // [batch][topk][inter]
     const int32_t *ids;
     const float *wt;
-    int32_t topk, S;
+    int32_t topk;
+    int32_t S;                         // waves per slot (K split)
+    int32_t spr;                       // slots per round
     void *y;                           // [batch][hidden]
     int32_t y_bf16;
 };
 
-constexpr int kDownPF = 8;
+// Tuning: K units (128 elements) per wave.
+#ifndef TT_DOWN_UPW
+#define TT_DOWN_UPW 8
+#endif
+constexpr int kDownOob = 0x7FFFFF00;
 
-template <bool HF32>
+__device__ __forceinline__ void down_lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// One workgroup per (16-row output tile, token).  Slots are processed in
+// rounds of spr; within a round wave (slot j, part p) owns units
+// [p * UPW, p * UPW + UPW) of expert ids[b][j]'s tile.  Issue order per wave:
+// its share of the round's activations, then each scale dword followed by its
+// four code units, then the postscales.  A slot with a bad expert id gets a
+// zero-length buffer descriptor, so its loads read nothing and return zeros.
+template <int UPW, bool HF32>
 __global__ __launch_bounds__(1024) void k_down_combine(DownArgs a) {
+    static_assert(UPW % 4 == 0 && UPW <= 16, "units per wave");
+    constexpr int ESZ = HF32 ? 4 : 2;
+    constexpr int XC = UPW * ESZ / 8;            // 16-byte chunks per thread per round
     extern __shared__ __align__(16) uint8_t smem[];
-    const int kp = a.units * 128;
-    const int esz = HF32 ? 4 : 2;
-    float *red = reinterpret_cast<float *>(smem + (size_t)a.topk * kp * esz);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int S = a.S, topk = a.topk, spr = a.spr;
+    const int kp = S * UPW * 128;                // staged K per slot, zero past inter
+    const int slot_chunks = kp * ESZ / 16;
+    uint4 *xs4 = reinterpret_cast<uint4 *>(smem);
+    float *red = reinterpret_cast<float *>(smem + (size_t)spr * kp * ESZ);  // [topk][S][16]
+    float *pss = red + topk * S * 16;                                       // [topk][17]
+    const int tid = threadIdx.x, lane = tid & 63, nthreads = blockDim.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tile = blockIdx.x, b = blockIdx.y;
-    const int nthreads = blockDim.x;
+    const int q = lane >> 4;
+    const int js = wave / S, part = wave - js * S;
+    const int valid_chunks = a.inter * ESZ / 16;
+    const uint4 *hsrc = reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(a.h) +
+                                                        (size_t)b * topk * a.inter * ESZ);
 
-    // stage h[b][0..topk-1] (zero-padded to kp each)
-    if (HF32) {
-        const float4 *src = reinterpret_cast<const float4 *>(
-            static_cast<const float *>(a.h) + (int64_t)b * a.topk * a.inter);
-        float4 *dst = reinterpret_cast<float4 *>(smem);
-        const int per = kp / 4, valid = a.inter / 4;
-        for (int i = tid; i < a.topk * per; i += nthreads) {
-            const int j = i / per, o = i % per;
-            dst[i] = (o < valid) ? src[j * valid + o] : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int jb = 0; jb < topk; jb += spr) {
+        const int j = jb + js;
+        const bool slot_ok = j < topk;
+        const int e = slot_ok ? a.ids[b * topk + j] : -1;
+        const bool valid = e >= 0 && e < a.n_experts;
+
+        // 1. activations of slots jb .. jb + spr - 1
+        uint4 hv[XC];
+#pragma unroll
+        for (int c = 0; c < XC; ++c) {
+            const int idx = tid + c * nthreads;
+            const int jj = jb + idx / slot_chunks, off = idx % slot_chunks;
+            hv[c] = (jj < topk && off < valid_chunks) ? hsrc[jj * valid_chunks + off]
+                                                     : make_uint4(0, 0, 0, 0);
         }
-    } else {
-        const uint16_t *src = static_cast<const uint16_t *>(a.h) + (int64_t)b * a.topk * a.inter;
-        for (int j = 0; j < a.topk; ++j)
-            stage_bf16(reinterpret_cast<uint16_t *>(smem) + j * kp, src + (int64_t)j * a.inter,
-                       a.inter, kp, tid, nthreads);
-    }
-    __syncthreads();
 
-    const int j = wave / a.S, part = wave % a.S;
-    const int e = a.ids[b * a.topk + j];
-    const bool valid = e >= 0 && e < a.n_experts;
-    const int r = lane & 15, q = lane >> 4;
-    float acc = 0.0f;
-    // postscale of this slot's expert for the tile's rows, fetched up front
-    float psj = 0.0f;
-    if (valid && part == 0 && lane < 16)
-        psj = reinterpret_cast<const float *>(a.bank + (int64_t)e * a.expert_stride +
-                                              (int64_t)tile * a.tile_stride + a.ps_off)[lane];
-    const float wj = a.wt[b * a.topk + j];
-    if (valid) {
-        const uint8_t *tb = a.bank + (int64_t)e * a.expert_stride + (int64_t)tile * a.tile_stride;
-        const uint8_t *sp = tb + a.scale_off + lane * 4;
-        const int upw = (a.units + a.S - 1) / a.S;
-        const int u0 = part * upw, u1 = min(a.units, u0 + upw);
-        for (int kb = u0; kb < u1; kb += kDownPF) {
-            uint4 c[kDownPF];
-            uint32_t s[kDownPF];
+        // 2. weights
+        const uint8_t *tb = valid ? a.bank + (int64_t)e * a.expert_stride +
+                                        (int64_t)tile * a.tile_stride
+                                  : a.bank;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t *>(tb), 0, valid ? (int)a.tile_stride : 0, 0x00020000);
+        const int u0 = part * UPW;
+        const int n = max(0, min(UPW, a.units - u0));
+        uint4 c[UPW];
+        uint32_t sd[UPW / 4];
+        const int voff = u0 * kUnitBytes + lane * 16;
+        const int soff = a.scale_off + (u0 >> 2) * kGroupBytes + lane * 4;
 #pragma unroll
-            for (int i = 0; i < kDownPF; ++i) {
-                const int kk = kb + i;
-                if (kk < u1) {
-                    const int off = kk * kUnitBytes +
-                                    ((kk == a.units - 1 && q >= a.qv_last) ? r * 16 : lane * 16);
-                    c[i] = *reinterpret_cast<const uint4 *>(tb + off);
-                    s[i] = *reinterpret_cast<const uint32_t *>(sp + (kk >> 2) * kGroupBytes);
-                }
-            }
+        for (int g = 0; g < UPW / 4; ++g) {
+            sd[g] = __builtin_amdgcn_raw_buffer_load_b32(
+                rs, 4 * g < n ? soff + g * kGroupBytes : kDownOob, 0, 0);
 #pragma unroll
-            for (int i = 0; i < kDownPF; ++i) {
-                const int kk = kb + i;
-                if (kk < u1) {
-                    const int blk = 4 * kk + q;
-                    float p;
-                    if (HF32)
-                        p = fp4x32_dot_f32(c[i], reinterpret_cast<const float4 *>(smem) +
-                                                     ((size_t)j * kp + blk * 32) / 4);
-                    else
-                        p = fp4x32_dot_bf16(c[i], reinterpret_cast<const uint4 *>(smem) +
-                                                      ((size_t)j * kp + blk * 32) / 8);
-                    acc = fmaf(p, e8m0_f32((s[i] >> (8 * (kk & 3))) & 255u), acc);
-                }
+            for (int i = 4 * g; i < 4 * g + 4; ++i) {
+                const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
+                    rs, i < n ? voff + i * kUnitBytes : kDownOob, 0, 0);
+                c[i] = make_uint4(v.x, v.y, v.z, v.w);
             }
         }
+        const float ps = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(
+                       rs, (part == 0 && lane < 16) ? a.ps_off + lane * 4 : kDownOob, 0, 0));
+        const float wj = slot_ok ? a.wt[b * topk + j] : 0.0f;
+
+        // 3. activations to LDS (after the previous round finished reading)
+        if (jb > 0) down_lds_barrier();
+#pragma unroll
+        for (int cc = 0; cc < XC; ++cc) {
+            const int idx = tid + cc * nthreads;
+            if (idx < spr * slot_chunks) xs4[idx] = hv[cc];
+        }
+        down_lds_barrier();
+
+        // 4. consume the units in load order
+        float acc = 0.0f;
+        if (HF32) {
+            const float4 *xb = reinterpret_cast<const float4 *>(smem) +
+                               ((size_t)js * kp + (4 * u0 + q) * 32) / 4;
+#pragma unroll
+            for (int i = 0; i < UPW; ++i)
+                acc = fmaf(fp4x32_dot_f32(c[i], xb + i * 32),
+                           e8m0_f32((sd[i >> 2] >> (8 * (i & 3))) & 255u), acc);
+        } else {
+            const uint4 *xb = xs4 + ((size_t)js * kp + (4 * u0 + q) * 32) / 8;
+#pragma unroll
+            for (int i = 0; i < UPW; ++i)
+                acc = fmaf(fp4x32_dot_bf16(c[i], xb + i * 16),
+                           e8m0_f32((sd[i >> 2] >> (8 * (i & 3))) & 255u), acc);
+        }
+        acc += __shfl_xor(acc, 16);
+        acc += __shfl_xor(acc, 32);
+        if (slot_ok) {
+            if (lane < 16) red[(j * S + part) * 16 + lane] = acc;
+            if (part == 0 && lane < 16) pss[j * 17 + lane] = ps;
+            if (part == 0 && lane == 16) pss[j * 17 + 16] = valid ? wj : __builtin_nanf("");
+        }
     }
-    acc += __shfl_xor(acc, 16);
-    acc += __shfl_xor(acc, 32);
-    // per slot: 16 postscales, then its routing weight (NaN marks a bad id)
-    float *pss = red + a.topk * a.S * 16;
-    if (lane < 16) red[wave * 16 + lane] = acc;
-    if (part == 0 && lane < 16) pss[j * 17 + lane] = psj;
-    if (part == 0 && lane == 16) pss[j * 17 + 16] = valid ? wj : __builtin_nanf("");
-    __syncthreads();
+    down_lds_barrier();
     if (wave != 0 || lane >= 16) return;
-    const int row = tile * 16 + lane;
+    // fixed order: parts, then slots j = 0 .. topk - 1; a bad id (NaN weight)
+    // makes the row NaN
     float y = 0.0f;
-    for (int jj = 0; jj < a.topk; ++jj) {
-        float dot = red[(jj * a.S) * 16 + lane];
-        for (int pp = 1; pp < a.S; ++pp) dot += red[(jj * a.S + pp) * 16 + lane];
+    for (int jj = 0; jj < topk; ++jj) {
+        float dot = red[(jj * S) * 16 + lane];
+        for (int pp = 1; pp < S; ++pp) dot += red[(jj * S + pp) * 16 + lane];
         y += pss[jj * 17 + 16] * (pss[jj * 17 + lane] * dot);
     }
+    const int row = tile * 16 + lane;
     if (row < a.hidden) store_out(a.y, (int64_t)b * a.hidden + row, y, a.y_bf16);
 }
 
+}  // namespace tt
+
+namespace tt {
+namespace {
+
+template <int UPW, bool HF32>
+tt_status launch_down(const DownArgs &a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+    if (lds > 64 * 1024) {
+        static bool raised[64] = {false};
+        int dev = 0;
+        (void)hipGetDevice(&dev);
+        if (dev >= 0 && dev < 64 && !raised[dev]) {
+            if (hipFuncSetAttribute(reinterpret_cast<const void *>(k_down_combine<UPW, HF32>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    160 * 1024) != hipSuccess)
+                return fail(TT_E_HIP, "cannot raise the LDS limit of the down kernel");
+            raised[dev] = true;
+        }
+    }
+    return launch("moe down + combine", k_down_combine<UPW, HF32>, grid, block, lds, s, a);
+}
+
+}  // namespace
 }  // namespace tt
 
 using namespace tt;
@@ -250,37 +317,33 @@ extern "C" tt_status tt_moe_mxfp4_down_combine(const void *down_bank, int64_t n_
     a.topk = (int32_t)topk;
     a.y = y;
     a.y_bf16 = y_dtype == TT_BF16;
-    // K-split per slot: up to 16 waves per workgroup in total
-    int S = 16 / (int)topk;
-    while (S > 1 && (int)ceil_div(g.units, S) < 4) S /= 2;
-    a.S = S < 1 ? 1 : S;
+    // waves per slot S = ceil(units / UPW), slots per round so that a
+    // workgroup holds at most 16 waves
+    int upw = TT_DOWN_UPW;
+    while (ceil_div(g.units, upw) > 16) upw += 4;
+    a.S = (int32_t)ceil_div(g.units, upw);
+    a.spr = (int32_t)std::max<int64_t>(1, std::min<int64_t>(topk, 16 / a.S));
     const size_t esz = h_dtype == TT_F32 ? 4 : 2;
-    const size_t lds = (size_t)topk * g.units * 128 * esz + (size_t)topk * a.S * 64 +
+    const size_t lds = (size_t)a.spr * a.S * upw * 128 * esz + (size_t)topk * a.S * 64 +
                        (size_t)topk * 17 * 4;
-    if (lds > 64 * 1024) {
-        static bool raised[2][64] = {{false}};
-        int dev = 0;
-        (void)hipGetDevice(&dev);
-        const int which = h_dtype == TT_F32;
-        if (dev >= 0 && dev < 64 && !raised[which][dev]) {
-            const void *fn = which ? reinterpret_cast<const void *>(k_down_combine<true>)
-                                   : reinterpret_cast<const void *>(k_down_combine<false>);
-            if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) !=
-                hipSuccess)
-                return fail(TT_E_HIP, "cannot raise the LDS limit of the down kernel");
-            raised[which][dev] = true;
-        }
-        if (lds > 160 * 1024)
-            return fail(TT_E_SHAPE, "topk * inter = %lld activations do not fit in LDS",
-                        (long long)(topk * inter));
-    }
+    if (lds > 160 * 1024)
+        return fail(TT_E_SHAPE, "inter = %lld: the staged activations do not fit in LDS",
+                    (long long)inter);
     dim3 grid((unsigned)ceil_div(hidden, kTileRows), (unsigned)batch);
-    dim3 block((unsigned)(64 * topk * a.S));
+    dim3 block((unsigned)(64 * a.S * a.spr));
     hipStream_t s = static_cast<hipStream_t>(stream);
-    tt_status st =
-        h_dtype == TT_F32
-            ? launch("moe down + combine", k_down_combine<true>, grid, block, lds, s, a)
-            : launch("moe down + combine", k_down_combine<false>, grid, block, lds, s, a);
+    tt_status st;
+    switch (upw * 2 + (h_dtype == TT_F32)) {
+        case 8: st = launch_down<4, false>(a, grid, block, lds, s); break;
+        case 9: st = launch_down<4, true>(a, grid, block, lds, s); break;
+        case 16: st = launch_down<8, false>(a, grid, block, lds, s); break;
+        case 17: st = launch_down<8, true>(a, grid, block, lds, s); break;
+        case 24: st = launch_down<12, false>(a, grid, block, lds, s); break;
+        case 25: st = launch_down<12, true>(a, grid, block, lds, s); break;
+        case 32: st = launch_down<16, false>(a, grid, block, lds, s); break;
+        default: st = launch_down<16, true>(a, grid, block, lds, s); break;
+    }
     if (st == TT_OK) clear_error();
     return st;
 }
+

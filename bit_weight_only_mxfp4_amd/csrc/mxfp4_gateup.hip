@@ -44,7 +44,59 @@ struct GateUpArgs {
     int32_t inter;
     int32_t batch;          // tokens (MFMA path)
     int32_t ks;             // waves per tile (vector path)
+    const uint16_t *logits; // fused routing: bf16 [tokens][n_experts], or NULL
+    int32_t *ids_out;       // fused routing: chosen experts [slots]
+    float *w_out;           // fused routing: routing weights [slots]
 };
+
+// Orderable key of (bf16 logit, expert index): larger logit first, then the
+// lower index; -0 folds onto +0 (the same ranking rule as the routing call).
+__device__ __forceinline__ uint32_t gu_route_key(uint32_t bits, int e) {
+    bits = (bits == 0x8000u) ? 0u : bits;
+    const uint32_t ord = (bits & 0x8000u) ? (~bits & 0xFFFFu) : (bits | 0x8000u);
+    return (ord << 16) | (0xFFFFu - (uint32_t)e);
+}
+
+// Expert of slot j for one token, computed by every wave of the workgroup from
+// the keys wave 0 wrote to LDS (keys past n_exp are 0, below every real key):
+// the expert whose key has exactly j larger keys.  Also returns the routing
+// weight, the softmax of the topk selected logits summed in rank order.
+__device__ __forceinline__ int gu_route_slot(const uint32_t *keys, const uint32_t *key,
+                                             const uint32_t *raw, int n_pad, int topk, int j,
+                                             int lane, float *wj) {
+    int rank[4] = {0, 0, 0, 0};
+    for (int e4 = 0; e4 < n_pad; e4 += 4) {
+        const uint4 k4 = *reinterpret_cast<const uint4 *>(keys + e4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            rank[i] += (k4.x > key[i]) + (k4.y > key[i]) + (k4.z > key[i]) + (k4.w > key[i]);
+    }
+    int e = 0;
+    float sel[TT_MAX_TOPK], selj = 0.0f;
+#pragma unroll
+    for (int r = 0; r < TT_MAX_TOPK; ++r) {
+        sel[r] = 0.0f;
+        if (r < topk) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint64_t m = __ballot(key[i] != 0u && rank[i] == r);
+                if (m) {
+                    const int src = __builtin_ctzll(m);
+                    sel[r] = bf16_bits_to_f32(__builtin_amdgcn_readlane(raw[i], src));
+                    if (r == j) e = src + 64 * i;
+                }
+            }
+            if (r == j) selj = sel[r];
+        }
+    }
+    float den = 0.0f;
+#pragma unroll
+    for (int r = 0; r < TT_MAX_TOPK; ++r)
+        if (r < topk) den += expf(sel[r] - sel[0]);
+    *wj = expf(selj - sel[0]) / den;
+    (void)lane;
+    return e;
+}
 
 // Tuning of the vector path: units of K per wave (4, 8, 12 or 16) and tiles
 // per workgroup.
@@ -54,6 +106,10 @@ struct GateUpArgs {
 #ifndef TT_GATEUP_TPB
 #define TT_GATEUP_TPB 2
 #endif
+#ifndef TT_GATEUP_MAXW
+#define TT_GATEUP_MAXW 8
+#endif
+constexpr int kMaxWavesPerTile = TT_GATEUP_MAXW;
 constexpr int kPF = 8;           // units in flight per wave (MFMA path)
 constexpr int kOob = 0x7FFFFF00; // buffer offset past every tile: loads return 0
 
@@ -93,7 +149,7 @@ __device__ __forceinline__ void lds_barrier() {
 // past the end of the pack, read at an out-of-range buffer offset and get
 // zeros, which contribute exactly nothing.
 template <int UPW, int TPB>
-__global__ __launch_bounds__(512) void k_gateup_valu(GateUpArgs a) {
+__global__ __launch_bounds__(1024) void k_gateup_valu(GateUpArgs a) {
     static_assert(UPW % 4 == 0 && UPW <= 16, "units per wave");
     extern __shared__ __align__(16) uint8_t smem[];
     const int ks = a.ks;
@@ -109,11 +165,46 @@ __global__ __launch_bounds__(512) void k_gateup_valu(GateUpArgs a) {
     const int tsub = wave / ks, part = wave - tsub * ks;
     const int tile = blockIdx.x * TPB + tsub, slot = blockIdx.y;
 
+    // routed calls have batch * topk slots; the dense call has one per token
+    const int tok = (a.ids || a.logits) ? slot / a.topk : slot;
+    // 1. activations: each thread fetches at most UPW / 4 chunks of 16 bytes
+    constexpr int XC = UPW / 4;  // nthreads * XC >= xchunks
+    const int xvalid = a.hidden / 8;
+    const uint4 *xg = reinterpret_cast<const uint4 *>(a.x + (int64_t)tok * a.hidden);
+    uint4 xv[XC];
+#pragma unroll
+    for (int j = 0; j < XC; ++j) {
+        const int idx = tid + j * nthreads;
+        xv[j] = idx < xvalid ? xg[idx] : make_uint4(0, 0, 0, 0);
+    }
+
+    // the expert id (routed call) is read after the activation loads are out
     const uint8_t *base = a.w;
-    int tok = slot;
-    if (a.ids) {
+    if (a.logits) {
+        // fused routing: rank the token's logits, pick slot j's expert
+        uint32_t *keys = reinterpret_cast<uint32_t *>(red + TPB * ks * 16);
+        const int n_pad = (a.n_experts + 3) & ~3;
+        const uint16_t *lb = a.logits + (int64_t)tok * a.n_experts;
+        uint32_t raw[4], key[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) raw[i] = lb[min(lane + 64 * i, a.n_experts - 1)];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ei = lane + 64 * i;
+            key[i] = ei < a.n_experts ? gu_route_key(raw[i], ei) : 0u;
+            if (wave == 0 && ei < n_pad) keys[ei] = key[i];
+        }
+        lds_barrier();
+        float wj;
+        const int j = slot - tok * a.topk;
+        const int e = gu_route_slot(keys, key, raw, n_pad, a.topk, j, lane, &wj);
+        if (blockIdx.x == 0 && tid == 0) {
+            a.ids_out[slot] = e;
+            a.w_out[slot] = wj;
+        }
+        base += (int64_t)e * a.expert_stride;
+    } else if (a.ids) {
         const int e = a.ids[slot];
-        tok = slot / a.topk;
         if (e < 0 || e >= a.n_experts) {
             for (int i = tid; i < TPB * 8; i += nthreads) {
                 const int pair = blockIdx.x * TPB * 8 + i;
@@ -124,17 +215,6 @@ __global__ __launch_bounds__(512) void k_gateup_valu(GateUpArgs a) {
             return;
         }
         base += (int64_t)e * a.expert_stride;
-    }
-
-    // 1. activations: each thread fetches at most UPW / 4 chunks of 16 bytes
-    constexpr int XC = UPW / 4;  // nthreads * XC >= xchunks
-    const int xvalid = a.hidden / 8;
-    const uint4 *xg = reinterpret_cast<const uint4 *>(a.x + (int64_t)tok * a.hidden);
-    uint4 xv[XC];
-#pragma unroll
-    for (int j = 0; j < XC; ++j) {
-        const int idx = tid + j * nthreads;
-        xv[j] = idx < xvalid ? xg[idx] : make_uint4(0, 0, 0, 0);
     }
 
     // 2. weights
@@ -295,7 +375,8 @@ template <int UPW>
 tt_status launch_valu_upw(GateUpArgs a, int slots, hipStream_t stream) {
     a.ks = (int32_t)ceil_div(a.units, UPW);
     const int tpb = (a.ks * TT_GATEUP_TPB <= 8) ? TT_GATEUP_TPB : 1;
-    const size_t lds = (size_t)a.ks * UPW * 256 + (size_t)tpb * a.ks * 64;
+    const size_t lds = (size_t)a.ks * UPW * 256 + (size_t)tpb * a.ks * 64 +
+                       (a.logits ? (size_t)TT_MAX_EXPERTS * 4 : 0);
     dim3 grid((unsigned)ceil_div(a.ntiles, tpb), (unsigned)slots);
     const char *what = "mxfp4 gate/up (vector path)";
     if (tpb == 1)
@@ -304,11 +385,12 @@ tt_status launch_valu_upw(GateUpArgs a, int slots, hipStream_t stream) {
                   stream, a);
 }
 
-// Units per wave: the tuned target, raised until a tile needs at most 8 waves
-// (K <= 16384 gives at most 128 units, so 16 units per wave always suffice).
+// Units per wave: the tuned target, raised until a tile needs at most
+// kMaxWavesPerTile waves (K <= 16384 gives at most 128 units, so 16 units per
+// wave always suffice).
 tt_status launch_valu(GateUpArgs a, int slots, hipStream_t stream) {
     int upw = TT_GATEUP_UPW;
-    while (ceil_div(a.units, upw) > 8) upw += 4;
+    while (ceil_div(a.units, upw) > kMaxWavesPerTile) upw += 4;
     switch (upw) {
         case 4: return launch_valu_upw<4>(a, slots, stream);
         case 8: return launch_valu_upw<8>(a, slots, stream);
@@ -367,6 +449,10 @@ GateUpArgs make_args(const void *w, int64_t inter, int64_t hidden, const void *x
     a.out_bf16 = out_dtype == TT_BF16;
     a.inter = (int32_t)inter;
     a.batch = 1;
+    a.ks = 1;
+    a.logits = nullptr;
+    a.ids_out = nullptr;
+    a.w_out = nullptr;
     return a;
 }
 
@@ -424,6 +510,32 @@ extern "C" tt_status tt_moe_mxfp4_gateup_swiglu(const void *bank, int64_t n_expe
     a.ids = ids;
     a.topk = (int32_t)topk;
     a.n_experts = (int32_t)n_experts;
+    tt_status st = launch_valu(a, (int)(batch * topk), static_cast<hipStream_t>(stream));
+    if (st == TT_OK) clear_error();
+    return st;
+}
+
+extern "C" tt_status tt_moe_mxfp4_route_gateup_swiglu(const void *bank, int64_t n_experts,
+                                                      int64_t inter, int64_t hidden,
+                                                      const void *x, int64_t batch,
+                                                      const void *logits, int64_t topk,
+                                                      int32_t *ids, float *w, void *h,
+                                                      int32_t h_dtype, void *stream) {
+    TT_TRY(check_gateup_common(bank, inter, hidden, x, batch, h, h_dtype));
+    TT_TRY(check_ptr(logits, "logits"));
+    TT_TRY(check_ptr(ids, "ids"));
+    TT_TRY(check_ptr(w, "w"));
+    TT_TRY(check_align(logits, 2, "logits"));
+    TT_TRY(check_align(ids, 4, "ids"));
+    TT_TRY(check_align(w, 4, "w"));
+    TT_TRY(check_range(n_experts, 1, TT_MAX_EXPERTS, "n_experts"));
+    TT_TRY(check_range(topk, 1, n_experts < TT_MAX_TOPK ? n_experts : TT_MAX_TOPK, "topk"));
+    GateUpArgs a = make_args(bank, inter, hidden, x, h, h_dtype);
+    a.topk = (int32_t)topk;
+    a.n_experts = (int32_t)n_experts;
+    a.logits = static_cast<const uint16_t *>(logits);
+    a.ids_out = ids;
+    a.w_out = w;
     tt_status st = launch_valu(a, (int)(batch * topk), static_cast<hipStream_t>(stream));
     if (st == TT_OK) clear_error();
     return st;

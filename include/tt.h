@@ -202,6 +202,21 @@ tt_status tt_moe_mxfp4_gateup_swiglu(const void *bank, int64_t n_experts,
                                      void *h, int32_t h_dtype, void *stream);
 
 /*
+ * Routing fused into the routed-expert gate/up: the same top-k selection and
+ * softmax weights as tt_moe_route_topk (bit-identical ids and weights),
+ * computed inside the gate/up kernel from the logits, followed by the same
+ * gate/up SwiGLU as tt_moe_mxfp4_gateup_swiglu.  Saves one launch per layer.
+ * logits: bf16 [batch][n_experts]; ids, w: outputs [batch][topk] (for the
+ * down projection); h: [batch][topk][inter] of h_dtype.
+ */
+tt_status tt_moe_mxfp4_route_gateup_swiglu(const void *bank, int64_t n_experts,
+                                           int64_t inter, int64_t hidden,
+                                           const void *x, int64_t batch,
+                                           const void *logits, int64_t topk,
+                                           int32_t *ids, float *w, void *h,
+                                           int32_t h_dtype, void *stream);
+
+/*
  * Routed-expert down projection and weighted combine:
  *   y[b][r] = sum_{j = 0..topk-1, in order} w[b][j] * ps_d[e][r] *
  *             sum_k Wd[e][r][k] * h[b][j][k],      e = ids[b][j]

@@ -101,6 +101,24 @@ def test_moe_layer_stages(dev, gptoss, batch, h_dtype):
     assert c >= 0.99999
 
 
+@pytest.mark.parametrize("batch", [1, 3])
+def test_fused_route_gateup_equals_separate_calls(dev, gptoss, batch):
+    w, n_exp = gptoss["w"], gptoss["n_exp"]
+    xd = dev_bf16(workloads.activations(w.wid, 2, batch, w.hidden), dev)
+    for step in range(3):
+        lg = workloads.router_logits(w.wid, 40 + step, batch, n_exp)
+        if step == 2:
+            lg[:, 1::2] = lg[:, 0::2]          # planted ties
+        lgd = dev_bf16(lg, dev)
+        ids, wt = tt.moe_route_topk(lgd, w.topk)
+        h = tt.moe_mxfp4_gateup_swiglu(gptoss["gu"], n_exp, w.inter, w.hidden, xd, ids)
+        hf, idf, wf = tt.moe_mxfp4_route_gateup_swiglu(gptoss["gu"], n_exp, w.inter, w.hidden,
+                                                       xd, lgd, w.topk)
+        assert torch.equal(idf, ids) and torch.equal(wf, wt) and torch.equal(hf, h)
+        rid, _ = oracle.moe_route_topk(lg, w.topk)
+        assert np.array_equal(idf.cpu().numpy(), rid)
+
+
 def test_moe_single_expert_equals_dense(dev, gptoss):
     w = gptoss["w"]
     x = workloads.activations(w.wid, 5, 1, w.hidden)
@@ -127,19 +145,28 @@ def test_moe_bad_ids_give_nan_rows(dev, gptoss):
     assert np.all(np.isnan(to_np(y)))
 
 
-def test_moe_down_ragged(dev):
-    """hidden not a multiple of 16, inter with a partial unit, topk 3."""
-    w = workloads.Workload(9, "rag", 96, 160, n_experts=5, topk=3)
+@pytest.mark.parametrize("hidden,inter,topk,h_bf16", [(96, 160, 3, False), (96, 160, 3, True),
+                                                      (40, 2048, 8, True), (48, 4096, 8, False),
+                                                      (33, 8192, 5, True)])
+def test_moe_down_ragged(dev, hidden, inter, topk, h_bf16):
+    """hidden not a multiple of 16, partial units, several slot rounds."""
+    n_exp = 9
+    w = workloads.Workload(9, "rag", hidden, inter, n_experts=n_exp, topk=topk)
     db = workloads.expert_bank(w, 0, "down")
-    dn = dev_u8(_down_pack(db, 5, w.hidden, w.inter), dev)
-    gen = np.random.default_rng(1)
-    h = gen.standard_normal((2, 3, w.inter)).astype(np.float32)
-    ids = np.array([[4, 0, 2], [1, 1, 3]], np.int32)
-    wt = np.array([[0.5, 0.3, 0.2], [0.6, 0.25, 0.15]], np.float32)
-    y = tt.moe_mxfp4_down_combine(dn, 5, w.hidden, w.inter, torch.from_numpy(h).to(dev),
+    dn = dev_u8(_down_pack(db, n_exp, w.hidden, w.inter), dev)
+    gen = np.random.default_rng(inter + topk)
+    h = gen.standard_normal((2, topk, w.inter)).astype(np.float32)
+    if h_bf16:
+        h = workloads.bf16_to_f32(workloads.bf16_bits(h))
+    ids = gen.integers(0, n_exp, (2, topk)).astype(np.int32)
+    wt = gen.uniform(0.05, 1.0, (2, topk)).astype(np.float32)
+    hd = torch.from_numpy(h).to(dev)
+    if h_bf16:
+        hd = hd.to(torch.bfloat16)
+    y = tt.moe_mxfp4_down_combine(dn, n_exp, w.hidden, w.inter, hd,
                                   torch.from_numpy(ids).to(dev), torch.from_numpy(wt).to(dev))
-    yr, S = oracle.moe_down_combine(db, 5, w.hidden, w.inter, h, ids, wt.astype(np.float64))
-    assert_parity(to_np(y), yr, gemv_tol(S, yr), "moe down ragged")
+    yr, S = oracle.moe_down_combine(db, n_exp, w.hidden, w.inter, h, ids, wt.astype(np.float64))
+    assert_parity(to_np(y), yr, gemv_tol(S, yr), f"moe down h{hidden} i{inter} k{topk}")
 
 
 # ---- INT4 ----------------------------------------------------------------------
