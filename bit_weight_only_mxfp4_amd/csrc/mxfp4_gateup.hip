@@ -18,9 +18,9 @@
 // SwiGLU run in registers.
 //
 // Batch 2..32 runs on MFMA (v_mfma_f32_16x16x32_bf16): the same 16-byte loads
-// become bf16 A operands with the block scale folded into the conversion,
-// the activations of up to 32 tokens are staged once per workgroup in LDS
-// and feed the B operands, and persistent workgroups walk the tiles.
+// become bf16 A operands with the block scale folded into the conversion, and
+// each wave keeps the activations of up to 32 tokens over its slice of K in
+// registers as B operands while it streams a run of tiles.
 #include <algorithm>
 
 #include "device.h"
@@ -282,75 +282,149 @@ __global__ __launch_bounds__(1024) void k_gateup_valu(GateUpArgs a) {
         store_out(a.out, (int64_t)slot * a.inter + pair, silu(y) * u, a.out_bf16);
 }
 
-// MFMA path.  NCOL column blocks of 16 tokens.  LDS row stride is padded by
-// 16 bytes so the 16 lanes of a B-operand read hit different banks.
-template <int NCOL>
-__global__ __launch_bounds__(512) void k_gateup_mfma(GateUpArgs a) {
+// MFMA path (batch 2..32).  NCOL column blocks of 16 tokens.  A workgroup of
+// 8 waves owns a contiguous run of at most TMAX tiles; wave p owns K-chunks
+// p, p + 8, ... of 2 units (256 elements) each.  For its K-chunk a wave copies
+// the activations of all tokens over those 256 elements into a private LDS
+// slice (direct buffer-to-LDS loads, one token row of 512 bytes per half
+// wave, rotated by the token index so the 16 tokens of a B operand fall on
+// different banks), reads its B operands from there once, and keeps them in
+// registers while it streams the weights of every tile of the run through
+// the matrix cores.  No workgroup barrier precedes the first MFMA.  The 8
+// partial tiles are then summed through LDS in a fixed order after one
+// barrier; the wave that finishes tile t (t = p) prefetched its postscales.
+constexpr int kMfmaWaves = 8;  // waves per workgroup = K-chunk stride
+constexpr int kMfmaUpc = 2;    // units per K-chunk
+
+template <int NCOL> constexpr int mfma_slice_bytes() { return NCOL * 16 * 512; }
+
+template <int NCOL, int TMAX>
+__global__ __launch_bounds__(64 * kMfmaWaves) void k_gateup_mfma(GateUpArgs a) {
+    static_assert(TMAX * NCOL * 1024 <= mfma_slice_bytes<NCOL>(), "partials fit the slice");
     extern __shared__ __align__(16) uint8_t smem[];
-    uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
-    const int rs = a.units * 128 + 8;  // bf16 elements per token row
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nw = blockDim.x >> 6;
-
-    for (int t = 0; t < a.batch; ++t)
-        stage_bf16(xs + t * rs, a.x + (int64_t)t * a.hidden, a.hidden, a.units * 128, tid,
-                   blockDim.x);
-    __syncthreads();
-
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int p = __builtin_amdgcn_readfirstlane(tid >> 6);
+    uint8_t *slice = smem + p * mfma_slice_bytes<NCOL>();
     const int r = lane & 15, q = lane >> 4;
-    for (int tile = blockIdx.x * nw + wave; tile < a.ntiles; tile += gridDim.x * nw) {
-        const uint8_t *tb = a.w + (int64_t)tile * a.tile_stride;
-        const uint8_t *sp = tb + a.scale_off + lane * 4;
-        // lane (token column, row group q) needs the postscales of rows 4q..4q+3
-        const float4 ps4 = reinterpret_cast<const float4 *>(tb + a.ps_off)[q];
-        f32x4_t C[NCOL];
+    const int nkc = (a.units + kMfmaUpc - 1) / kMfmaUpc;
+    // balanced split of the tiles over the workgroups: at most TMAX each
+    const int t0 = (int)((int64_t)blockIdx.x * a.ntiles / gridDim.x);
+    const int nt = (int)((int64_t)(blockIdx.x + 1) * a.ntiles / gridDim.x) - t0;
+    const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(a.x, (int64_t)a.batch * a.hidden * 2);
+
+    f32x4_t C[TMAX][NCOL];
 #pragma unroll
-        for (int cb = 0; cb < NCOL; ++cb) C[cb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        for (int kb = 0; kb < a.units; kb += kPF) {
-            uint4 c[kPF];
-            uint32_t s[kPF];
+    for (int t = 0; t < TMAX; ++t)
 #pragma unroll
-            for (int i = 0; i < kPF; ++i) {
-                const int kk = kb + i;
-                if (kk < a.units) {
-                    c[i] = *reinterpret_cast<const uint4 *>(
-                        tb + code_off(kk, lane, a.units, a.qv_last));
-                    s[i] = *reinterpret_cast<const uint32_t *>(sp + (kk >> 2) * kGroupBytes);
+        for (int cb = 0; cb < NCOL; ++cb) C[t][cb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4_t ps4 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int kc = p; kc < nkc; kc += kMfmaWaves) {  // one round unless K > 2048
+        const int u0 = kc * kMfmaUpc;
+        // 1. activations of the K-chunk into the slice: instruction i covers
+        //    tokens 2i and 2i+1; slot s of token t holds 16-byte piece
+        //    (s - t) mod 32; zeros past the batch and past K
+        //    (token pairs past the batch are skipped: their slots only feed
+        //    output columns that are never stored)
+#pragma unroll
+        for (int i = 0; i < NCOL * 8; ++i) {
+            if (2 * i >= a.batch) break;
+            const int t = 2 * i + (lane >> 5), pc = ((lane & 31) - t) & 31;
+            const int k = u0 * 128 + 8 * pc;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                xr, (__attribute__((address_space(3))) void *)(slice + i * 1024), 16,
+                (t < a.batch && k < a.hidden) ? (t * a.hidden + k) * 2 : kOob, 0, 0, 0);
+        }
+        // 2. postscales of rows 4q .. 4q+3 of tile p, which this wave finishes
+        //    (issued before the weights: completion is in order, and the
+        //    epilogue must not wait on a load of its own)
+        if (kc == p) {
+            const bool ok = p < nt;
+            const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(
+                a.w + (int64_t)(ok ? t0 + p : 0) * a.tile_stride, ok ? a.tile_stride : 0);
+            ps4 = __builtin_bit_cast(
+                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, a.ps_off + 16 * q, 0, 0));
+        }
+        // 3. weights of every tile of the run: the units' scale dword, then
+        //    the two units; tiles past the run read zeros
+        uint4 c[TMAX][kMfmaUpc];
+        uint32_t sd[TMAX];
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) {
+            const bool ok = t < nt;
+            const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(
+                a.w + (int64_t)(ok ? t0 + t : 0) * a.tile_stride, ok ? a.tile_stride : 0);
+            sd[t] = __builtin_amdgcn_raw_buffer_load_b32(
+                rs, a.scale_off + (u0 >> 2) * kGroupBytes + lane * 4, 0, 0);
+#pragma unroll
+            for (int u = 0; u < kMfmaUpc; ++u)
+                c[t][u] = load16(rs, u0 + u < a.units ? code_off(u0 + u, lane, a.units, a.qv_last)
+                                                      : kOob);
+        }
+        // keep every load above this point: the scheduler would otherwise
+        // sink the last ones past the first MFMAs and add a round trip
+        __builtin_amdgcn_sched_barrier(0);
+        // 4. B operands from the slice: lane (r, q) takes token cb*16 + r at
+        //    elements (4u + q)*32 + 8j .. +8, i.e. piece (4u + q)*4 + j
+        uint4 xb[kMfmaUpc][4][NCOL];
+#pragma unroll
+        for (int u = 0; u < kMfmaUpc; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int cb = 0; cb < NCOL; ++cb) {
+                    const int t = cb * 16 + r, pc = (4 * u + q) * 4 + j;
+                    xb[u][j][cb] =
+                        *reinterpret_cast<const uint4 *>(slice + t * 512 + ((pc + t) & 31) * 16);
                 }
-            }
+        // 5. tile by tile, each as soon as its loads land
 #pragma unroll
-            for (int i = 0; i < kPF; ++i) {
-                const int kk = kb + i;
-                if (kk < a.units) {
-                    const float sc = e8m0_f32((s[i] >> (8 * (kk & 3))) & 255u);
-                    const uint32_t cw[4] = {c[i].x, c[i].y, c[i].z, c[i].w};
-                    const int kbase = (4 * kk + q) * 32;
+        for (int t = 0; t < TMAX; ++t) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const bf16x8_t A = fp4x8_to_bf16x8(cw[j], sc);
+            for (int u = 0; u < kMfmaUpc; ++u) {
+                const float sc = e8m0_f32((sd[t] >> (8 * ((u0 + u) & 3))) & 255u);
+                const uint32_t cw[4] = {c[t][u].x, c[t][u].y, c[t][u].z, c[t][u].w};
 #pragma unroll
-                        for (int cb = 0; cb < NCOL; ++cb) {
-                            const uint4 xb = *reinterpret_cast<const uint4 *>(
-                                xs + (cb * 16 + r) * rs + kbase + 8 * j);
-                            C[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                A, __builtin_bit_cast(bf16x8_t, xb), C[cb], 0, 0, 0);
-                        }
-                    }
+                for (int j = 0; j < 4; ++j) {
+                    const bf16x8_t A = fp4x8_to_bf16x8(cw[j], sc);
+#pragma unroll
+                    for (int cb = 0; cb < NCOL; ++cb)
+                        C[t][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            A, __builtin_bit_cast(bf16x8_t, xb[u][j][cb]), C[t][cb], 0, 0, 0);
                 }
             }
         }
-        // lane (token column r, row group q) holds rows 4q..4q+3 of the tile
-        const float psv[4] = {ps4.x, ps4.y, ps4.z, ps4.w};
+    }
+
+    // 6. partial tiles into the wave's own slice (its B operands are in
+    //    registers by now), one barrier, fixed-order sum by the finisher
+    const int nparts = min(kMfmaWaves, nkc);
+    if (p < nparts) {
+        f32x4_t *red = reinterpret_cast<f32x4_t *>(slice);
 #pragma unroll
-        for (int cb = 0; cb < NCOL; ++cb) {
+        for (int t = 0; t < TMAX; ++t)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const float y = C[cb][t] * psv[t];
-                const float u = __shfl_down(y, 32);
-                const int token = cb * 16 + r, pair = tile * 8 + 4 * q + t;
-                if (lane < 32 && token < a.batch && pair < a.inter)
-                    store_out(a.out, (int64_t)token * a.inter + pair, silu(y) * u, a.out_bf16);
-            }
+            for (int cb = 0; cb < NCOL; ++cb)
+                if (t < nt) red[(t * NCOL + cb) * 64 + lane] = C[t][cb];
+    }
+    lds_barrier();
+    if (p >= nt) return;
+    const int tile = t0 + p;
+#pragma unroll
+    for (int cb = 0; cb < NCOL; ++cb) {
+        const f32x4_t *red = reinterpret_cast<const f32x4_t *>(smem) + (p * NCOL + cb) * 64 + lane;
+        constexpr int kStride = mfma_slice_bytes<NCOL>() / 16;
+        f32x4_t y = red[0];
+        for (int s = 1; s < nparts; ++s) y += red[s * kStride];
+        // lane (token column r, row group q) holds rows 4q..4q+3 of the tile:
+        // gate rows in lanes 0..31, the matching up rows 32 lanes on
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float g = y[i] * ps4[i];
+            const float u = __shfl_down(g, 32);
+            const int token = cb * 16 + r, pair = tile * 8 + 4 * q + i;
+            if (lane < 32 && token < a.batch && pair < a.inter)
+                store_out(a.out, (int64_t)token * a.inter + pair, silu(g) * u, a.out_bf16);
         }
     }
 }
@@ -402,29 +476,34 @@ tt_status launch_valu(GateUpArgs a, int slots, hipStream_t stream) {
 
 constexpr size_t kMaxLds = 160 * 1024;
 
-size_t mfma_lds(const GateUpArgs &a, int ncol) {
-    return (size_t)ncol * 16 * ((size_t)a.units * 128 + 8) * 2;
-}
+// Tiles per workgroup run: the weights of the whole run are in flight in
+// registers at once, and a wave's partial tiles fit its activation slice.
+template <int NCOL> constexpr int mfma_tmax() { return NCOL == 1 ? 3 : 6; }
+
+size_t mfma_lds(int ncol) { return (size_t)kMfmaWaves * ncol * 16 * 512; }
 
 template <int NCOL>
 tt_status launch_mfma(const GateUpArgs &a, hipStream_t stream) {
-    const size_t lds = mfma_lds(a, NCOL);
+    constexpr int TMAX = mfma_tmax<NCOL>();
+    const size_t lds = mfma_lds(NCOL);
     static bool attr_set[64] = {false};
     int dev = 0;
     (void)hipGetDevice(&dev);
     if (lds > 64 * 1024 && dev >= 0 && dev < 64 && !attr_set[dev]) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(k_gateup_mfma<NCOL>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(k_gateup_mfma<NCOL, TMAX>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)kMaxLds) != hipSuccess)
             return fail(TT_E_HIP, "cannot raise the LDS limit of the MFMA gate/up kernel");
         attr_set[dev] = true;
     }
-    const int per_cu = (int)(kMaxLds / lds);
-    const int waves = 8;
-    int blocks = (int)ceil_div(a.ntiles, waves);
-    blocks = min(blocks, device_cus() * max(per_cu, 1));
-    return launch("mxfp4 gate/up (MFMA path)", k_gateup_mfma<NCOL>, dim3(blocks),
-                  dim3(64 * waves), lds, stream, a);
+    // as many workgroups as fit the CUs at once (two with 16 tokens, one with
+    // 32), never more than TMAX tiles per workgroup (the split in the kernel
+    // is balanced): shorter runs put more waves on each SIMD
+    const int64_t per_cu = std::min<int64_t>(2, (int64_t)(kMaxLds / lds));
+    const int64_t blocks = std::max<int64_t>(
+        std::min<int64_t>(a.ntiles, per_cu * device_cus()), ceil_div(a.ntiles, TMAX));
+    return launch("mxfp4 gate/up (MFMA path)", k_gateup_mfma<NCOL, TMAX>, dim3((unsigned)blocks),
+                  dim3(64 * kMfmaWaves), lds, stream, a);
 }
 
 GateUpArgs make_args(const void *w, int64_t inter, int64_t hidden, const void *x,
@@ -487,12 +566,10 @@ extern "C" tt_status tt_mxfp4_gateup_swiglu(const void *w_gu, int64_t inter, int
     tt_status st;
     if (batch == 1)
         st = launch_valu(a, 1, s);
-    else if (batch <= 16 && mfma_lds(a, 1) <= kMaxLds)
+    else if (batch <= 16)
         st = launch_mfma<1>(a, s);
-    else if (mfma_lds(a, 2) <= kMaxLds)
-        st = launch_mfma<2>(a, s);
     else
-        st = launch_valu(a, (int)batch, s);  // one weight pass per token
+        st = launch_mfma<2>(a, s);
     if (st == TT_OK) clear_error();
     return st;
 }

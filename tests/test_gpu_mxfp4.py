@@ -134,6 +134,19 @@ def test_batched_smollm3_sampled_rows(dev, batch):
     assert_parity(got, ref["h"], h_tol(ref), f"batched b{batch}")
 
 
+# MFMA path off the SmolLM3 shape: ragged last unit (qv_last < 4), two chunks
+# per tile, a single unit, tiles past the grid (each wave walks several
+# tiles), and widths that fall back to one weight pass per token.
+@pytest.mark.parametrize("hidden,inter,batch", [(2880, 1000, 5), (4096, 520, 9), (2336, 1000, 32),
+                                                (96, 100, 3), (32, 8, 2), (5120, 24, 4),
+                                                (2048, 20000, 32), (2048, 11008, 23)])
+def test_batched_ragged_shapes(dev, hidden, inter, batch):
+    w = workloads.Workload(9, "ragged", hidden, inter)
+    rows = _sample_rows(inter, 64, batch) if inter > 2048 else None
+    got, ref = _gateup_case(dev, w, 0, batch, rows=rows)
+    assert_parity(got, ref["h"], h_tol(ref), f"batched ragged h{hidden} i{inter} b{batch}")
+
+
 @pytest.mark.parametrize("batch", [1, 8])
 def test_bf16_output(dev, batch):
     w = workloads.Workload(9, "bf16", 512, 300)
