@@ -29,6 +29,7 @@ struct I4Args {
     int32_t y_bf16;
     int32_t ks;         // waves per tile
     int32_t xvec;       // x rows are 16-byte aligned (k % 8 == 0 and x aligned)
+                        // and batch * k * 2 fits a buffer range
 };
 
 // Tuning: units (128-element groups) per wave; a tile uses at most 16 waves.
@@ -39,15 +40,24 @@ constexpr int kOob = 0x7FFFFF00;  // buffer offset past every tile: loads return
 
 // (128 + q) x summed over the 8 codes of one dword; xg holds the reordered
 // activation pairs of that 8-element group.
-__device__ __forceinline__ float i4x8_dot(uint32_t c, uint4 xg, float acc) {
-    const uint32_t m = 0x000F000Fu, bias = 0x43004300u;
-    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2((c & m) | bias), as_bf16x2(xg.x), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(((c >> 4) & m) | bias), as_bf16x2(xg.y), acc,
+// (x & m) | b in one VALU op (the compiler otherwise emits an AND and an OR:
+// VOP3 on this target reads at most one scalar, so b stays in a VGPR)
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t b) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(b));
+    return r;
+}
+
+__device__ __forceinline__ float i4x8_dot(uint32_t c, uint4 xg, float acc, uint32_t bias) {
+    const uint32_t m = 0x000F000Fu;
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(and_or(c, m, bias)), as_bf16x2(xg.x), acc,
                                           false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(((c >> 8) & m) | bias), as_bf16x2(xg.z), acc,
-                                          false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(((c >> 12) & m) | bias), as_bf16x2(xg.w), acc,
-                                          false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(and_or(c >> 4, m, bias)), as_bf16x2(xg.y),
+                                          acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(and_or(c >> 8, m, bias)), as_bf16x2(xg.z),
+                                          acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(and_or(c >> 12, m, bias)), as_bf16x2(xg.w),
+                                          acc, false);
     return acc;
 }
 
@@ -67,7 +77,7 @@ __device__ __forceinline__ void i4_lds_barrier() {
 // pieces, then each s|z group followed by its four code units.  Units past K
 // read at an out-of-range buffer offset (zeros) and meet zero-padded
 // activations and zero piece sums, so they add exactly nothing.
-template <int UPW, int NT>
+template <int UPW, int NT, bool XVEC>
 __global__ __launch_bounds__(1024) void k_int4_gemv(I4Args a) {
     static_assert(UPW % 4 == 0 && UPW <= 16, "units per wave");
     extern __shared__ __align__(16) uint8_t smem[];
@@ -82,21 +92,24 @@ __global__ __launch_bounds__(1024) void k_int4_gemv(I4Args a) {
     const int tile = blockIdx.x, t0 = blockIdx.y * NT;
     const int nt = min(NT, a.batch - t0);
 
-    // 1. activations: thread tid fetches piece tid of every token
+    // 1. activations: thread tid fetches piece tid of every token.  Rows of
+    //    16-byte aligned x go out as straight-line buffer loads (zeros past
+    //    the batch and past k), so the weight loads follow without a wait;
+    //    other rows take element loads.
     uint32_t xw[NT][16];
-    const bool xvec = a.xvec != 0;
     {
         const int p = tid;
+        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(a.x), 0, XVEC ? a.batch * a.k * 2 : 0, 0x00020000);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const uint16_t *src = a.x + (int64_t)(t0 + t) * a.k + p * 32;
             const bool tok_ok = t < nt;
-            if (xvec) {
+            if (XVEC) {
 #pragma unroll
                 for (int g8 = 0; g8 < 4; ++g8) {
                     const bool ok = tok_ok && p * 32 + g8 * 8 < a.k;
-                    const uint4 v = ok ? reinterpret_cast<const uint4 *>(src)[g8]
-                                       : make_uint4(0, 0, 0, 0);
+                    const uint4 v = i4_load16(xr, ok ? ((t0 + t) * a.k + p * 32 + g8 * 8) * 2 : kOob);
                     xw[t][4 * g8 + 0] = v.x;
                     xw[t][4 * g8 + 1] = v.y;
                     xw[t][4 * g8 + 2] = v.z;
@@ -113,6 +126,10 @@ __global__ __launch_bounds__(1024) void k_int4_gemv(I4Args a) {
             }
         }
     }
+
+    // keep the activation loads ahead of the weights (completion is in
+    // order: the staging below then waits for the activations only)
+    __builtin_amdgcn_sched_barrier(0);
 
     // 2. weights
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -161,6 +178,7 @@ __global__ __launch_bounds__(1024) void k_int4_gemv(I4Args a) {
     float acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = 0.0f;
+    const uint32_t bias = 0x43004300u;
 #pragma unroll
     for (int i = 0; i < UPW; ++i) {
         const uint32_t sz = (i & 3) == 0 ? szv[i >> 2].x
@@ -172,10 +190,10 @@ __global__ __launch_bounds__(1024) void k_int4_gemv(I4Args a) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const uint4 *xg = reinterpret_cast<const uint4 *>(xs + t * kp + p * 32);
-            float d0 = i4x8_dot(c[i].x, xg[0], 0.0f);
-            float d1 = i4x8_dot(c[i].y, xg[1], 0.0f);
-            d0 = i4x8_dot(c[i].z, xg[2], d0);
-            d1 = i4x8_dot(c[i].w, xg[3], d1);
+            float d0 = i4x8_dot(c[i].x, xg[0], 0.0f, bias);
+            float d1 = i4x8_dot(c[i].y, xg[1], 0.0f, bias);
+            d0 = i4x8_dot(c[i].z, xg[2], d0, bias);
+            d1 = i4x8_dot(c[i].w, xg[3], d1, bias);
             acc[t] = fmaf(s, fmaf(-zb, xsum[t * pieces + p], d0 + d1), acc[t]);
         }
     }
@@ -218,8 +236,9 @@ template <int UPW, int NT>
 tt_status launch_i4(I4Args a, hipStream_t s) {
     a.ks = (int32_t)ceil_div(a.units, UPW);
     dim3 grid(a.ntiles, (a.batch + NT - 1) / NT);
-    return launch("int4 gemv", k_int4_gemv<UPW, NT>, grid, dim3(64 * a.ks),
-                  lds_bytes(a.ks, UPW, NT), s, a);
+    const size_t lds = lds_bytes(a.ks, UPW, NT);
+    return a.xvec ? launch("int4 gemv", k_int4_gemv<UPW, NT, true>, grid, dim3(64 * a.ks), lds, s, a)
+                  : launch("int4 gemv", k_int4_gemv<UPW, NT, false>, grid, dim3(64 * a.ks), lds, s, a);
 }
 
 template <int UPW>
@@ -272,7 +291,8 @@ extern "C" tt_status tt_int4_gemv(const void *w_packed, int64_t n, int64_t k, in
     a.batch = (int32_t)batch;
     a.y = y;
     a.y_bf16 = y_dtype == TT_BF16;
-    a.xvec = (k % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0);
+    a.xvec = (k % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+             batch * k * 2 < (int64_t)kOob;
     hipStream_t s = static_cast<hipStream_t>(stream);
     int upw = TT_INT4_UPW;
     while (ceil_div(a.units, upw) > 16) upw += 4;
