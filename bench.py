@@ -15,7 +15,8 @@ with us_per_call, the roofline of the kernel and the CPU oracle timed on the
 host (a reported baseline, not a target).
 
 Other workloads (--workload): tiny, phi4 (gate/up), phi4-int4 (QKV + O),
-gptoss (route + expert gate/up + down/combine), batched (--batch B).
+gptoss (routing fused into the expert gate/up, then down/combine), batched
+(--batch B).
 """
 from __future__ import annotations
 
@@ -260,9 +261,10 @@ def run(args):
         h = torch.empty((1, w.topk, w.inter), dtype=torch.bfloat16, device=dev)
         y = torch.empty((1, w.hidden), dtype=torch.float32, device=dev)
         def step():
+            # routing fused into the expert gate/up call, then down + combine
             for li, (g_, d_) in enumerate(banks):
-                tt.moe_route_topk(logits[li], w.topk, ids=ids, w=wt)
-                tt.moe_mxfp4_gateup_swiglu(g_, E, w.inter, w.hidden, x, ids, out=h)
+                tt.moe_mxfp4_route_gateup_swiglu(g_, E, w.inter, w.hidden, x, logits[li], w.topk,
+                                                 ids=ids, w=wt, out=h)
                 tt.moe_mxfp4_down_combine(d_, E, w.hidden, w.inter, h, ids, wt, out=y)
 
         secs = time_graph(torch, capture(torch, step), K, W)
@@ -277,9 +279,10 @@ def run(args):
                       ms_per_step=round(secs / K * 1e3, 4),
                       config=dict(workload=w.name, hidden=w.hidden, inter=w.inter, experts=E,
                                   topk=w.topk, batch=1, layers_rotated=layers, h_dtype="bf16",
-                                  routing="a distinct seeded routing per layer",
+                                  routing="a distinct seeded routing per layer, fused into "
+                                          "the expert gate/up call",
                                   launch="one HIP graph per step"),
-                      roofline=dict(bound="hbm", kernel="k_route_topk+k_gateup_valu+k_down_combine",
+                      roofline=dict(bound="hbm", kernel="k_gateup_valu(routed)+k_down_combine",
                                     achieved=round(gbs, 2), peak=PEAK_HBM_GBS, unit="GB/s",
                                     frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
     else:

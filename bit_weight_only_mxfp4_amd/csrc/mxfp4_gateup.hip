@@ -57,44 +57,43 @@ __device__ __forceinline__ uint32_t gu_route_key(uint32_t bits, int e) {
     return (ord << 16) | (0xFFFFu - (uint32_t)e);
 }
 
-// Expert of slot j for one token, computed by every wave of the workgroup from
-// the keys wave 0 wrote to LDS (keys past n_exp are 0, below every real key):
-// the expert whose key has exactly j larger keys.  Also returns the routing
-// weight, the softmax of the topk selected logits summed in rank order.
-__device__ __forceinline__ int gu_route_slot(const uint32_t *keys, const uint32_t *key,
-                                             const uint32_t *raw, int n_pad, int topk, int j,
-                                             int lane, float *wj) {
-    int rank[4] = {0, 0, 0, 0};
-    for (int e4 = 0; e4 < n_pad; e4 += 4) {
-        const uint4 k4 = *reinterpret_cast<const uint4 *>(keys + e4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            rank[i] += (k4.x > key[i]) + (k4.y > key[i]) + (k4.z > key[i]) + (k4.w > key[i]);
-    }
-    int e = 0;
+// Expert of slot j for one token, by iterated wave maxima over the keys of
+// the token's logits (4 per lane; keys past the expert count are 0, below
+// every real key).  A key carries both its logit and its expert index, so
+// rank r's logit and expert come straight out of the r-th maximum.  With
+// want_w the routing weight follows: the softmax of the topk selected logits,
+// summed in rank order.  No LDS and no barrier: every wave does this itself.
+__device__ __forceinline__ int gu_route_topj(uint32_t key[4], int topk, int j, bool want_w,
+                                             float *wj) {
+    const int need = want_w ? topk : j + 1;
     float sel[TT_MAX_TOPK], selj = 0.0f;
+    int e = 0;
 #pragma unroll
     for (int r = 0; r < TT_MAX_TOPK; ++r) {
         sel[r] = 0.0f;
-        if (r < topk) {
+        if (r < need) {
+            uint32_t m = max(max(key[0], key[1]), max(key[2], key[3]));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint64_t m = __ballot(key[i] != 0u && rank[i] == r);
-                if (m) {
-                    const int src = __builtin_ctzll(m);
-                    sel[r] = bf16_bits_to_f32(__builtin_amdgcn_readlane(raw[i], src));
-                    if (r == j) e = src + 64 * i;
-                }
+            for (int off = 32; off >= 1; off >>= 1)
+                m = max(m, (uint32_t)__shfl_xor((int)m, off));
+            const uint32_t ord = m >> 16;
+            const uint32_t bits = (ord & 0x8000u) ? (ord & 0x7FFFu) : (~ord & 0xFFFFu);
+            sel[r] = bf16_bits_to_f32(bits);
+            if (r == j) {
+                e = (int)(0xFFFFu - (m & 0xFFFFu));
+                selj = sel[r];
             }
-            if (r == j) selj = sel[r];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) key[i] = key[i] == m ? 0u : key[i];
         }
     }
-    float den = 0.0f;
+    if (want_w) {
+        float den = 0.0f;
 #pragma unroll
-    for (int r = 0; r < TT_MAX_TOPK; ++r)
-        if (r < topk) den += expf(sel[r] - sel[0]);
-    *wj = expf(selj - sel[0]) / den;
-    (void)lane;
+        for (int r = 0; r < TT_MAX_TOPK; ++r)
+            if (r < topk) den += expf(sel[r] - sel[0]);
+        *wj = expf(selj - sel[0]) / den;
+    }
     return e;
 }
 
@@ -181,24 +180,24 @@ __global__ __launch_bounds__(1024) void k_gateup_valu(GateUpArgs a) {
     // the expert id (routed call) is read after the activation loads are out
     const uint8_t *base = a.w;
     if (a.logits) {
-        // fused routing: rank the token's logits, pick slot j's expert
-        uint32_t *keys = reinterpret_cast<uint32_t *>(red + TPB * ks * 16);
-        const int n_pad = (a.n_experts + 3) & ~3;
+        // fused routing: slot j's expert from the token's logits; the
+        // workgroups of tile 0 also produce the routing outputs
         const uint16_t *lb = a.logits + (int64_t)tok * a.n_experts;
-        uint32_t raw[4], key[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) raw[i] = lb[min(lane + 64 * i, a.n_experts - 1)];
+        uint32_t key[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int ei = lane + 64 * i;
-            key[i] = ei < a.n_experts ? gu_route_key(raw[i], ei) : 0u;
-            if (wave == 0 && ei < n_pad) keys[ei] = key[i];
+            key[i] = 0u;
+            if (64 * i < a.n_experts) {  // uniform
+                const uint32_t raw = lb[min(ei, a.n_experts - 1)];
+                key[i] = ei < a.n_experts ? gu_route_key(raw, ei) : 0u;
+            }
         }
-        lds_barrier();
-        float wj;
+        float wj = 0.0f;
         const int j = slot - tok * a.topk;
-        const int e = gu_route_slot(keys, key, raw, n_pad, a.topk, j, lane, &wj);
-        if (blockIdx.x == 0 && tid == 0) {
+        const bool writer = blockIdx.x == 0;
+        const int e = gu_route_topj(key, a.topk, j, writer, &wj);
+        if (writer && tid == 0) {
             a.ids_out[slot] = e;
             a.w_out[slot] = wj;
         }
@@ -449,8 +448,7 @@ template <int UPW>
 tt_status launch_valu_upw(GateUpArgs a, int slots, hipStream_t stream) {
     a.ks = (int32_t)ceil_div(a.units, UPW);
     const int tpb = (a.ks * TT_GATEUP_TPB <= 8) ? TT_GATEUP_TPB : 1;
-    const size_t lds = (size_t)a.ks * UPW * 256 + (size_t)tpb * a.ks * 64 +
-                       (a.logits ? (size_t)TT_MAX_EXPERTS * 4 : 0);
+    const size_t lds = (size_t)a.ks * UPW * 256 + (size_t)tpb * a.ks * 64;
     dim3 grid((unsigned)ceil_div(a.ntiles, tpb), (unsigned)slots);
     const char *what = "mxfp4 gate/up (vector path)";
     if (tpb == 1)
