@@ -231,7 +231,10 @@ def run(args):
                                   launch="one HIP graph per step"),
                       roofline=dict(bound="hbm", kernel="k_int4_gemv", achieved=round(gbs, 2),
                                     peak=PEAK_HBM_GBS, unit="GB/s",
-                                    frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
+                                    frac=round(gbs / PEAK_HBM_GBS, 4),
+                                    traffic=profiled_traffic(
+                                        ("int4_gemv.hip", "device.h", "layout.h"),
+                                        "int4_phi4_qkv_o.md")))
 
     elif args.workload == "gptoss":
         w = workloads.GPTOSS
@@ -284,7 +287,10 @@ def run(args):
                                   launch="one HIP graph per step"),
                       roofline=dict(bound="hbm", kernel="k_gateup_valu(routed)+k_down_combine",
                                     achieved=round(gbs, 2), peak=PEAK_HBM_GBS, unit="GB/s",
-                                    frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
+                                    frac=round(gbs / PEAK_HBM_GBS, 4),
+                                    traffic=profiled_traffic(
+                                        ("mxfp4_gateup.hip", "moe.hip", "device.h", "layout.h"),
+                                        "moe_gptoss_layer.md")))
     else:
         raise SystemExit(f"unknown workload {args.workload}")
 
