@@ -68,6 +68,7 @@ def lib() -> ctypes.CDLL:
                                             I64, P, I64, P, I64, P, P, P]),
             "or_moe_down_combine": (None, [P, P, P, I64, I64, I64, P, P, P, I64,
                                            I64, P, I64, P, P]),
+            "or_mxfp4_quantize": (ctypes.c_int, [P, I64, I64, P, P, P]),
             "or_int4_quantize": (ctypes.c_int, [P, I64, I64, I64, P, P, P]),
             "or_int4_dequantize": (None, [P, P, P, I64, I64, I64, P]),
             "or_int4_gemv": (None, [P, P, P, I64, I64, I64, P, I64, P, I64, P, P]),
@@ -214,6 +215,23 @@ def moe_down_combine(d_bank, n_exp, hidden, inter, h, ids, w, rows=None):
 
 
 # ---- INT4 ---------------------------------------------------------------
+
+def mxfp4_quantize(w, fit_postscale=True):
+    """fp32 [N][K] -> (codes u8[N][K/2], scales u8[N][K/32], ps f32[N] or
+    None): the OCP MX shared-exponent rule, then the least-squares row
+    postscale when fit_postscale."""
+    w = _c(w, np.float32)
+    n, k = w.shape
+    if k % 32:
+        raise ValueError("K must be a multiple of 32")
+    codes = np.empty((n, k // 2), np.uint8)
+    scales = np.empty((n, k // 32), np.uint8)
+    ps = np.empty(n, np.float32) if fit_postscale else None
+    rc = lib().or_mxfp4_quantize(_p(w), n, k, _p(codes), _p(scales), _p(ps))
+    if rc != 0:
+        raise ValueError("non-finite input")
+    return codes, scales, ps
+
 
 def int4_quantize(w, group=128):
     """Returns (q packed u8[N][K/2], s u16[N][G], z u16[N][G])."""

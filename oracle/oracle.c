@@ -383,6 +383,97 @@ void or_moe_down_combine(const uint8_t *d_codes, const uint8_t *d_scales,
 }
 
 /* ------------------------------------------------------------------ */
+/* MXFP4 quantizer                                                     */
+/* ------------------------------------------------------------------ */
+
+/* Nearest E2M1 code (magnitude index 0..7) of a >= 0: ties go to the even
+ * index, magnitudes at or above 6 clamp to 6 [OCP, conversion of a vector
+ * of scalars to an MX block: round to nearest even, clamp to the largest
+ * normal element]. */
+static int e2m1_nearest_index(double a)
+{
+    static const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    if (a >= 6.0)
+        return 7;
+    for (int i = 0; i < 7; ++i) {
+        if (a < grid[i + 1]) {
+            double below = a - grid[i], above = grid[i + 1] - a;
+            if (below < above)
+                return i;
+            if (above < below)
+                return i + 1;
+            return (i % 2 == 0) ? i : i + 1;
+        }
+    }
+    return 7;
+}
+
+/*
+ * MXFP4 quantizer [OCP]: per block of 32 consecutive k of a row, the shared
+ * scale is X = 2^(floor(log2(max |V|)) - 2) -- 2 being the exponent of the
+ * largest normal E2M1 magnitude, 6 = 1.5 * 2^2 -- with the exponent clamped
+ * to the E8M0 range [-127, 127] (an all-zero block takes 2^-127, byte 0);
+ * each element is V / X rounded to the nearest E2M1 value, ties to the even
+ * code, magnitudes above 6 clamped to 6, the sign kept (a negative value
+ * that rounds to zero is -0, code 8).
+ *
+ * Then, when ps is not NULL, the row postscale: the pages apply one per
+ * quantized row but do not say how it is chosen; the reading taken is the
+ * least-squares fit of the row, ps = <w, d> / <d, d> over the decoded row d
+ * (exact products code * X), fp64 sums in k order, rounded to fp32; 1 when
+ * d is all zero.
+ *
+ * Returns 0, or -1 (nothing written) when an input is not finite.
+ */
+int or_mxfp4_quantize(const float *w, int64_t n, int64_t k, uint8_t *codes,
+                      uint8_t *scales, float *ps)
+{
+    int64_t nb = k / 32;
+    for (int64_t i = 0; i < n * k; ++i)
+        if (!isfinite(w[i]))
+            return -1;
+    memset(codes, 0, (size_t)(n * (k / 2)));
+    for (int64_t r = 0; r < n; ++r) {
+        double wd = 0.0, dd = 0.0;
+        for (int64_t b = 0; b < nb; ++b) {
+            const float *v = w + r * k + 32 * b;
+            double amax = 0.0;
+            int e;
+            for (int j = 0; j < 32; ++j)
+                if (fabs((double)v[j]) > amax)
+                    amax = fabs((double)v[j]);
+            if (amax == 0.0) {
+                e = -127;
+            } else {
+                int ex;
+                frexp(amax, &ex);      /* amax = m * 2^ex, m in [0.5, 1) */
+                e = (ex - 1) - 2;      /* floor(log2(amax)) - 2 */
+                if (e < -127)
+                    e = -127;
+                if (e > 127)
+                    e = 127;
+            }
+            scales[r * nb + b] = (uint8_t)(e + 127);
+            for (int j = 0; j < 32; ++j) {
+                double x = ldexp((double)v[j], -e);   /* exact */
+                int idx = e2m1_nearest_index(fabs(x));
+                int code = idx | (signbit(x) ? 8 : 0);
+                int64_t kk = 32 * b + j;
+                codes[r * (k / 2) + kk / 2] |= (uint8_t)((kk & 1) ? code << 4 : code);
+                if (ps) {
+                    double d = or_e2m1_value(code) * ldexp(1.0, e);
+                    wd += (double)v[j] * d;
+                    dd += d * d;
+                }
+            }
+        }
+        if (ps)
+            ps[r] = dd == 0.0 ? 1.0f : (float)(wd / dd);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* Grouped affine INT4                                                 */
 /* ------------------------------------------------------------------ */
 
