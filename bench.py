@@ -291,6 +291,35 @@ def run(args):
                                     traffic=profiled_traffic(
                                         ("mxfp4_gateup.hip", "moe.hip", "device.h", "layout.h"),
                                         "moe_gptoss_layer.md")))
+    elif args.workload == "quantize":
+        # host-side MXFP4 quantizer + postscale fit on one SmolLM3-shaped
+        # layer's fp32 gate and up rows (a host function: no GPU work)
+        w = workloads.SMOLLM3
+        gen = np.random.default_rng([0, 99])
+        wg = (0.02 * gen.standard_normal((w.inter, w.hidden))).astype(np.float32)
+        wu = (0.02 * gen.standard_normal((w.inter, w.hidden))).astype(np.float32)
+        tt.quantize_mxfp4(wg)
+        t0 = time.perf_counter()
+        for _ in range(K):
+            tt.quantize_mxfp4(wg)
+            tt.quantize_mxfp4(wu)
+        secs = time.perf_counter() - t0
+        nbytes = 2 * wg.nbytes
+        gbs = nbytes * K / secs / 1e9
+        result = dict(metric="host MXFP4 quantizer + row-postscale fit throughput (fp32 in)",
+                      value=round(gbs, 3), unit="GB/s", ms_per_step=round(secs / K * 1e3, 3),
+                      config=dict(workload="smollm3-3b-gateup-quantize", rows=2 * w.inter,
+                                  k=w.hidden, threads=1),
+                      roofline=None)
+        if not args.no_cpu_baseline:
+            import oracle
+            t0 = time.perf_counter()
+            oracle.mxfp4_quantize(wg)
+            oracle.mxfp4_quantize(wu)
+            osecs = time.perf_counter() - t0
+            result["cpu_baseline"] = dict(value=round(nbytes / osecs / 1e9, 3), unit="GB/s",
+                                          cores=1, kind="oracle",
+                                          sample="one layer's gate and up rows, single thread")
     else:
         raise SystemExit(f"unknown workload {args.workload}")
 
@@ -327,7 +356,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="smollm3",
-                    choices=["smollm3", "tiny", "phi4", "phi4-int4", "gptoss", "batched"])
+                    choices=["smollm3", "tiny", "phi4", "phi4-int4", "gptoss", "batched",
+                             "quantize"])
     ap.add_argument("--batch", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)

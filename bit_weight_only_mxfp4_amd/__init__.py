@@ -40,6 +40,7 @@ _SIGS = {
     "tt_pack_mxfp4_matrix": (_I32, [_P, _P, _P, _I64, _I64, _P, _I64]),
     "tt_mxfp4_gateup_pack_bytes": (_I64, [_I64, _I64]),
     "tt_pack_mxfp4_gateup": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _P, _I64]),
+    "tt_quantize_mxfp4": (_I32, [_P, _I64, _I64, _P, _P, _P]),
     "tt_quantize_int4_affine": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "tt_int4_pack_bytes": (_I64, [_I64, _I64, _I64]),
     "tt_pack_int4": (_I32, [_P, _P, _P, _I64, _I64, _I64, _P, _I64]),
@@ -140,6 +141,20 @@ def pack_mxfp4_gateup(g, u, inter, hidden, out=None):
                                     _np_ptr(us), _np_ptr(up), inter, hidden, _np_ptr(dst),
                                     dst.nbytes))
     return dst
+
+
+def quantize_mxfp4(w, fit_postscale: bool = True):
+    """fp32 [n][k] -> (codes u8[n][k/2], scales u8[n][k/32], ps f32[n] or
+    None): MXFP4 blocks by the OCP shared-exponent rule, then the
+    least-squares row postscale when fit_postscale."""
+    w = _host(w, np.float32)
+    n, k = w.shape
+    codes = np.empty((n, k // 2), np.uint8)
+    scales = np.empty((n, max(k // 32, 1)), np.uint8)
+    ps = np.empty(n, np.float32) if fit_postscale else None
+    _check(lib.tt_quantize_mxfp4(_np_ptr(w), n, k, _np_ptr(codes), _np_ptr(scales),
+                                 _np_ptr(ps) if ps is not None else None))
+    return codes, scales, ps
 
 
 def quantize_int4_affine(w, group: int = INT4_GROUP):

@@ -1,6 +1,9 @@
 // pack.cpp -- host-side packers (canonical -> tiled device layout) and the
 // affine INT4 quantizer.  Pure CPU code, caller-owned buffers.
 #include <math.h>
+
+#include <algorithm>
+#include <cmath>
 #include <string.h>
 
 #include "layout.h"
@@ -167,6 +170,66 @@ tt_status tt_pack_mxfp4_gateup(const uint8_t *g_codes, const uint8_t *g_scales,
             p[i + 8] = ok ? (u_ps ? u_ps[row] : 1.0f) : 0.0f;
         }
         pack_mx_tile(g, crow, srow, p, out + t * g.stride);
+    }
+    clear_error();
+    return TT_OK;
+}
+
+// E2M1 rounding by midpoints: the index of the nearest of the magnitudes
+// 0, 0.5, 1, 1.5, 2, 3, 4, 6 is the number of midpoints below a, where a
+// value sitting on a midpoint counts it only if the index above is even
+// (ties to the even code); everything from 5 up (past the last midpoint)
+// lands on 6.
+static int fp4_index(double a) {
+    static const double mid[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+    int idx = 0;
+    for (int i = 0; i < 7; ++i) idx += (a > mid[i]) || (a == mid[i] && ((i + 1) & 1) == 0);
+    return idx;
+}
+
+tt_status tt_quantize_mxfp4(const float *w, int64_t n, int64_t k, uint8_t *codes,
+                            uint8_t *scales, float *ps) {
+    TT_TRY(check_ptr(w, "w"));
+    TT_TRY(check_ptr(codes, "codes"));
+    TT_TRY(check_ptr(scales, "scales"));
+    TT_TRY(check_range(n, 1, TT_MAX_ROWS, "n"));
+    TT_TRY(check_range(k, 32, TT_MAX_K, "k"));
+    if (k % 32) return fail(TT_E_SHAPE, "k = %lld is not a multiple of 32", (long long)k);
+    for (int64_t i = 0; i < n * k; ++i)
+        if (!std::isfinite(w[i]))
+            return fail(TT_E_RANGE, "w[%lld][%lld] is not finite", (long long)(i / k),
+                        (long long)(i % k));
+    static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    const int64_t nb = k / 32;
+    for (int64_t r = 0; r < n; ++r) {
+        const float *row = w + r * k;
+        double num = 0.0, den = 0.0;
+        for (int64_t b = 0; b < nb; ++b) {
+            const float *v = row + 32 * b;
+            float amax = 0.0f;
+            for (int j = 0; j < 32; ++j) amax = std::fmax(amax, std::fabs(v[j]));
+            int e = amax == 0.0f ? -127 : std::ilogb(amax) - 2;
+            e = std::min(127, std::max(-127, e));
+            scales[r * nb + b] = static_cast<uint8_t>(e + 127);
+            const double inv = std::ldexp(1.0, -e), sc = std::ldexp(1.0, e);
+            uint8_t *crow = codes + r * (k / 2) + 16 * b;
+            for (int j = 0; j < 32; j += 2) {
+                uint8_t byte = 0;
+                for (int h = 0; h < 2; ++h) {
+                    const double x = static_cast<double>(v[j + h]) * inv;  // exact
+                    const int idx = fp4_index(std::fabs(x));
+                    const bool neg = std::signbit(x);
+                    byte |= static_cast<uint8_t>((idx | (neg ? 8 : 0)) << (4 * h));
+                    if (ps) {
+                        const double d = (neg ? -mag[idx] : mag[idx]) * sc;
+                        num += static_cast<double>(v[j + h]) * d;
+                        den += d * d;
+                    }
+                }
+                crow[j / 2] = byte;
+            }
+        }
+        if (ps) ps[r] = den == 0.0 ? 1.0f : static_cast<float>(num / den);
     }
     clear_error();
     return TT_OK;

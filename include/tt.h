@@ -131,6 +131,28 @@ tt_status tt_pack_mxfp4_gateup(const uint8_t *g_codes, const uint8_t *g_scales,
                                void *dst, int64_t dst_bytes);
 
 /*
+ * MXFP4 quantizer (the stardance page, "ThinTensor Improvements": MXFP4
+ * quantizers; the conversion rule is the OCP MX v1.0 specification's, for a
+ * vector of scalars to an MX block).  For every row and every block of 32
+ * consecutive k (k a multiple of 32):
+ *   e      = floor(log2(max |w|)) - 2, clamped to [-127, 127]; an all-zero
+ *            block takes e = -127 (scale byte 0)
+ *   scale  = E8M0 byte e + 127
+ *   code_k = nearest FP4 E2M1 value of w_k / 2^e, ties to the even code,
+ *            magnitudes above 6 clamped to 6, sign kept (-0 is code 8)
+ * codes are written [n][k/2] (element 2j in the low nibble of byte j),
+ * scales [n][k/32].  When ps is not NULL it receives the row postscale the
+ * Dev Log #4 profile enables ("MXFP4 row postscale: enabled"); the pages do
+ * not say how it is chosen, so it is the least-squares fit of the row,
+ * ps = <w, d> / <d, d> over the decoded row d (fp64 sums in k order, rounded
+ * to fp32; 1 when d is zero).  Host function; all buffers are host memory
+ * owned by the caller.  TT_E_RANGE (nothing written) if an input is not
+ * finite.
+ */
+tt_status tt_quantize_mxfp4(const float *w, int64_t n, int64_t k, uint8_t *codes,
+                            uint8_t *scales, float *ps);
+
+/*
  * Affine INT4 quantizer ("Implemented a huge list of fixes": affine INT4 with
  * a correct partial last group).  For every row and every group of `group`
  * (= 128) consecutive k -- the last group holding what is left of k -- over

@@ -182,3 +182,45 @@ def test_int4_pack_layout():
                     seg = q[row, 16 * p:16 * p + 16]
                     want[:seg.size] = seg
                     assert np.array_equal(got, want)
+
+
+def _quant_inputs(n, k, seed):
+    gen = np.random.default_rng(seed)
+    w = (gen.standard_normal((n, k)) * np.exp2(gen.integers(-20, 20, (n, 1)))).astype(np.float32)
+    w[0, :32] = 0.0                                   # all-zero block
+    w[1, :8] = [5, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 4]  # ties
+    w[1, 8] = -0.0
+    w[1, 9] = -0.01                                   # rounds to -0
+    if n > 2:
+        w[2, :2] = [3e38, -1e38]                      # near the fp32 top
+    if n > 3:
+        w[3, :2] = [1e-40, -2e-41]                    # fp32 subnormals
+    return w
+
+
+@pytest.mark.parametrize("n,k,fit", [(5, 32, True), (37, 256, True), (64, 2048, False),
+                                     (3, 2880, True)])
+def test_mxfp4_quantizer_matches_oracle_bit_for_bit(n, k, fit):
+    w = _quant_inputs(n, k, n + k)
+    c1, s1, p1 = tt.quantize_mxfp4(w, fit_postscale=fit)
+    c2, s2, p2 = oracle.mxfp4_quantize(w, fit_postscale=fit)
+    assert np.array_equal(c1, c2)
+    assert np.array_equal(s1, s2)
+    if fit:
+        assert np.array_equal(p1.view(np.uint32), p2.view(np.uint32))
+    else:
+        assert p1 is None and p2 is None
+
+
+def test_mxfp4_quantizer_errors_write_nothing():
+    w = np.ones((2, 64), np.float32)
+    w[1, 40] = np.nan
+    codes = np.full((2, 32), 0xAB, np.uint8)
+    scales = np.full((2, 2), 0xCD, np.uint8)
+    rc = tt.lib.tt_quantize_mxfp4(w.ctypes.data, 2, 64, codes.ctypes.data, scales.ctypes.data,
+                                  None)
+    assert rc == -6
+    assert np.all(codes == 0xAB) and np.all(scales == 0xCD)
+    rc = tt.lib.tt_quantize_mxfp4(w.ctypes.data, 2, 48, codes.ctypes.data, scales.ctypes.data,
+                                  None)
+    assert rc == -2
