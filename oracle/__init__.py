@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
             "or_moe_down_combine": (None, [P, P, P, I64, I64, I64, P, P, P, I64,
                                            I64, P, I64, P, P]),
             "or_mxfp4_quantize": (ctypes.c_int, [P, I64, I64, P, P, P]),
+            "or_fp8e4m3_value": (D, [ctypes.c_int]),
+            "or_fp8_gemv": (None, [P, P, I64, I64, P, ctypes.c_int, I64, P, I64, P, P]),
             "or_int4_quantize": (ctypes.c_int, [P, I64, I64, I64, P, P, P]),
             "or_int4_dequantize": (None, [P, P, P, I64, I64, I64, P]),
             "or_int4_gemv": (None, [P, P, P, I64, I64, I64, P, I64, P, I64, P, P]),
@@ -215,6 +217,28 @@ def moe_down_combine(d_bank, n_exp, hidden, inter, h, ids, w, rows=None):
 
 
 # ---- INT4 ---------------------------------------------------------------
+
+def fp8e4m3_value(code):
+    return lib().or_fp8e4m3_value(int(code))
+
+
+def fp8_gemv(w, scale, n, k, x, rows=None):
+    """y[b][r] = scale[r] * sum_k w[r][k] x[b][k] (E4M3 bytes w [n][k];
+    x bf16 bit patterns (uint16) or fp32).  Returns (y, S), fp64
+    [batch][len(rows) or n]."""
+    w = _c(w, np.uint8)
+    scale = _c(scale, np.float32)
+    x = np.asarray(x)
+    x_f32 = 1 if x.dtype == np.float32 else 0
+    x = _c(x, np.float32 if x_f32 else np.uint16).reshape(-1, k)
+    batch = x.shape[0]
+    r = None if rows is None else _c(rows, np.int64)
+    m = n if r is None else r.size
+    y = np.empty((batch, m), np.float64)
+    S = np.empty((batch, m), np.float64)
+    lib().or_fp8_gemv(_p(w), _p(scale), n, k, _p(x), x_f32, batch, _p(r), m, _p(y), _p(S))
+    return y, S
+
 
 def mxfp4_quantize(w, fit_postscale=True):
     """fp32 [N][K] -> (codes u8[N][K/2], scales u8[N][K/32], ps f32[N] or

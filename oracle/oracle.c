@@ -31,6 +31,9 @@
  *          "numerical drift & speedups" (selected-expert MXFP4 matvec,
  *          dense INT4 Q/K/V/O), "Implemented a huge list of fixes" (affine
  *          INT4 with a partial last group).
+ *   [OCP FP8] OCP 8-bit Floating Point Specification (OFP8): the E4M3
+ *          encoding (bias 7, no infinities, S.1111.111 = NaN).  The pages
+ *          say "FP8" only; E4M3 is the reading taken for weights.
  *   [OCP]  OCP Microscaling Formats (MX) Specification v1.0: the FP4 E2M1
  *          element (1 sign, 2 exponent bits with bias 1, 1 mantissa bit) and
  *          the E8M0 shared scale (2^(e-127), 0xFF = NaN), 32 elements per
@@ -380,6 +383,64 @@ void or_moe_down_combine(const uint8_t *d_codes, const uint8_t *d_scales,
         }
     }
     free(wr);
+}
+
+/* ------------------------------------------------------------------ */
+/* FP8 row-scaled matvec                                               */
+/* ------------------------------------------------------------------ */
+
+/* FP8 E4M3 value of a byte [OCP FP8, the E4M3 encoding without
+ * infinities]: bit 7 sign, bits 6..3 exponent (bias 7), bits 2..0
+ * mantissa; exponent 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN. */
+double or_fp8e4m3_value(int code)
+{
+    int sign = (code >> 7) & 1;
+    int expo = (code >> 3) & 15;
+    int mant = code & 7;
+    double mag;
+    if (expo == 15 && mant == 7)
+        return NAN;
+    if (expo == 0)
+        mag = ldexp(mant / 8.0, -6);
+    else
+        mag = ldexp(1.0 + mant / 8.0, expo - 7);
+    return sign ? -mag : mag;
+}
+
+/*
+ * Row-scaled FP8 matvec ([DL3], the scaled FP8 matvec of the quality FP8
+ * profile: the row's sum of weight * activation, activations and scale in
+ * fp32, times the row scale):
+ *   y[b][r] = scale[r] * sum_k w[r][k] * x[b][k]
+ * w: E4M3 bytes [n][k]; scale f32 [n] (NULL = ones); x: bf16 bit patterns
+ * (x_f32 = 0) or fp32 (x_f32 = 1) [batch][k].  Products and sums in fp64,
+ * one row at a time.  rows (NULL = all n) selects output rows; y and S are
+ * [batch][nrows], S = |scale| * sum |w x| (the error scale of the sum).
+ */
+void or_fp8_gemv(const uint8_t *w, const float *scale, int64_t n, int64_t k,
+                 const void *x, int x_f32, int64_t batch, const int64_t *rows,
+                 int64_t nrows, double *y, double *S)
+{
+    int64_t m = rows ? nrows : n;
+    double *xv = (double *)malloc((size_t)(batch * k) * sizeof(double));
+    for (int64_t i = 0; i < batch * k; ++i)
+        xv[i] = x_f32 ? (double)((const float *)x)[i]
+                      : or_bf16_value(((const uint16_t *)x)[i]);
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t i = 0; i < m; ++i) {
+            int64_t r = rows ? rows[i] : i;
+            double sc = scale ? (double)scale[r] : 1.0, acc = 0.0, mag = 0.0;
+            for (int64_t j = 0; j < k; ++j) {
+                double p = or_fp8e4m3_value(w[r * k + j]) * xv[b * k + j];
+                acc += p;
+                mag += fabs(p);
+            }
+            y[b * m + i] = sc * acc;
+            if (S)
+                S[b * m + i] = fabs(sc) * mag;
+        }
+    }
+    free(xv);
 }
 
 /* ------------------------------------------------------------------ */
