@@ -16,7 +16,8 @@ host (a reported baseline, not a target).
 
 Other workloads (--workload): tiny, phi4 (gate/up), phi4-int4 (QKV + O),
 gptoss (routing fused into the expert gate/up, then down/combine), batched
-(--batch B).
+(--batch B), fp8-down (row-scaled FP8 down projection), quantize (host MXFP4
+quantizer).
 """
 from __future__ import annotations
 
@@ -291,6 +292,38 @@ def run(args):
                                     traffic=profiled_traffic(
                                         ("mxfp4_gateup.hip", "moe.hip", "device.h", "layout.h"),
                                         "moe_gptoss_layer.md")))
+    elif args.workload == "fp8-down":
+        # the dense down projection of the SmolLM3-shaped MLP as a row-scaled
+        # FP8 matvec on the gate/up SwiGLU output h (fp32), batch 1
+        n, k, layers = 2048, 11008, 24
+        log(f"setup FP8 down [{n}x{k}], {layers} layers")
+        packs = []
+        for layer in range(4):
+            codes, scale = workloads.fp8_matrix(1, layer, n, k)
+            packs.append(torch.from_numpy(tt.pack_fp8_matrix(codes, scale, n, k)).to(dev))
+        while len(packs) < layers:
+            packs.append(packs[len(packs) % 4].clone())
+        h = torch.from_numpy(workloads.swiglu_like(1, 0, 1, k)).to(dev)
+        y = torch.empty((1, n), dtype=torch.float32, device=dev)
+
+        def step():
+            for p in packs:
+                tt.fp8_gemv(p, n, k, h, out=y)
+
+        secs = time_graph(torch, capture(torch, step), K, W)
+        calls = K * layers
+        per_call = n * k + n * 4 + k * 4 + n * 4
+        gbs = per_call * calls / secs / 1e9
+        result = dict(metric="effective HBM GB/s of the row-scaled FP8 E4M3 down projection",
+                      value=round(gbs, 2), unit="GB/s", us_per_call=round(secs / calls * 1e6, 3),
+                      ms_per_step=round(secs / K * 1e3, 4), bytes_per_call=per_call,
+                      config=dict(workload="smollm3-3b-fp8-down-h2048-i11008", n=n, k=k,
+                                  batch=1, x="fp32 SwiGLU output", layers_rotated=layers,
+                                  launch="one HIP graph per step"),
+                      roofline=dict(bound="hbm", kernel="k_fp8_gemv", achieved=round(gbs, 2),
+                                    peak=PEAK_HBM_GBS, unit="GB/s",
+                                    frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
+
     elif args.workload == "quantize":
         # host-side MXFP4 quantizer + postscale fit on one SmolLM3-shaped
         # layer's fp32 gate and up rows (a host function: no GPU work)
@@ -323,8 +356,12 @@ def run(args):
     else:
         raise SystemExit(f"unknown workload {args.workload}")
 
+    dtype = {"phi4-int4": "int4 x bf16 -> fp32 accumulate",
+             "fp8-down": "fp8-e4m3 x fp32 -> fp32 accumulate",
+             "quantize": "fp32 -> fp4-e2m1 + e8m0 (host)"}.get(
+                 args.workload, "fp4-e2m1 x bf16 -> fp32 accumulate")
     result.update(n_gpus=1, steps=K, warmup=W, higher_is_better=True, scaling="strong",
-                  vs_baseline=None, dtype="fp4-e2m1 x bf16 -> fp32 accumulate",
+                  vs_baseline=None, dtype=dtype,
                   data="synthetic (seeded codes, scales, postscales, activations)")
     if "cpu_baseline" not in result:
         result["cpu_baseline"] = None
@@ -357,7 +394,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="smollm3",
                     choices=["smollm3", "tiny", "phi4", "phi4-int4", "gptoss", "batched",
-                             "quantize"])
+                             "fp8-down", "quantize"])
     ap.add_argument("--batch", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)

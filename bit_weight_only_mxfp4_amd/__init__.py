@@ -43,6 +43,8 @@ _SIGS = {
     "tt_quantize_mxfp4": (_I32, [_P, _I64, _I64, _P, _P, _P]),
     "tt_quantize_int4_affine": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "tt_int4_pack_bytes": (_I64, [_I64, _I64, _I64]),
+    "tt_fp8_pack_bytes": (_I64, [_I64, _I64]),
+    "tt_pack_fp8_matrix": (_I32, [_P, _P, _I64, _I64, _P, _I64]),
     "tt_pack_int4": (_I32, [_P, _P, _P, _I64, _I64, _I64, _P, _I64]),
     "tt_mxfp4_gateup_swiglu": (_I32, [_P, _I64, _I64, _P, _I64, _P, _I32, _P]),
     "tt_moe_route_topk": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P]),
@@ -53,9 +55,11 @@ _SIGS = {
     "tt_moe_mxfp4_down_combine": (_I32, [_P, _I64, _I64, _I64, _P, _I32, _P, _P, _I64,
                                          _I64, _P, _I32, _P]),
     "tt_int4_gemv": (_I32, [_P, _I64, _I64, _I64, _P, _I64, _P, _I32, _P]),
+    "tt_fp8_gemv": (_I32, [_P, _I64, _I64, _P, _I32, _I64, _P, _I32, _P]),
     "tt_mxfp4_dequantize": (_I32, [_P, _I64, _I64, _P, _P, _P]),
     "tt_mxfp4_gateup_dequantize": (_I32, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
     "tt_int4_dequantize": (_I32, [_P, _I64, _I64, _I64, _P, _P]),
+    "tt_fp8_dequantize": (_I32, [_P, _I64, _I64, _P, _P, _P]),
 }
 
 # libtt.so needs libamdhip64.so.7.  torch bundles its own HIP runtime under that
@@ -140,6 +144,20 @@ def pack_mxfp4_gateup(g, u, inter, hidden, out=None):
     _check(lib.tt_pack_mxfp4_gateup(_np_ptr(gc), _np_ptr(gs), _np_ptr(gp), _np_ptr(uc),
                                     _np_ptr(us), _np_ptr(up), inter, hidden, _np_ptr(dst),
                                     dst.nbytes))
+    return dst
+
+
+def fp8_pack_bytes(n: int, k: int) -> int:
+    return _size(lib.tt_fp8_pack_bytes(n, k))
+
+
+def pack_fp8_matrix(codes, scale, n, k, out=None):
+    """Canonical FP8 E4M3 codes u8[n][k] and row scales f32[n] (or None) ->
+    packed uint8 numpy array (or into ``out``)."""
+    c, sc = _host(codes, np.uint8), _host(scale, np.float32)
+    nbytes = fp8_pack_bytes(n, k)
+    dst = np.empty(nbytes, np.uint8) if out is None else out
+    _check(lib.tt_pack_fp8_matrix(_np_ptr(c), _np_ptr(sc), n, k, _np_ptr(dst), dst.nbytes))
     return dst
 
 
@@ -310,6 +328,20 @@ def int4_gemv(w_packed, n, k, x, group=INT4_GROUP, out=None, out_dtype=None):
     return out
 
 
+def fp8_gemv(w_packed, n, k, x, out=None, out_dtype=None):
+    """y[b][r] = scale[r] * sum_k w[r][k] x[b][k] for x [batch][k] fp32 or
+    bf16 (e.g. the gate/up SwiGLU output h)."""
+    torch = _torch()
+    _dev_ptr(x, "x", (torch.float32, torch.bfloat16))
+    batch = x.numel() // k
+    if out is None:
+        out = torch.empty((batch, n), dtype=out_dtype or torch.float32, device=x.device)
+    _check(lib.tt_fp8_gemv(_dev_ptr(w_packed, "w_packed", (torch.uint8,)), n, k,
+                           _dev_ptr(x, "x"), _dtype_code(x.dtype), batch, _dev_ptr(out, "y"),
+                           _dtype_code(out.dtype), _stream(x)))
+    return out
+
+
 def mxfp4_dequantize(packed, n, k):
     torch = _torch()
     w = torch.empty((n, k), dtype=torch.float32, device=packed.device)
@@ -336,6 +368,15 @@ def int4_dequantize(packed, n, k, group=INT4_GROUP):
     _check(lib.tt_int4_dequantize(_dev_ptr(packed, "packed", (torch.uint8,)), n, k, group,
                                   _dev_ptr(w, "w"), _stream(packed)))
     return w
+
+
+def fp8_dequantize(packed, n, k):
+    torch = _torch()
+    w = torch.empty((n, k), dtype=torch.float32, device=packed.device)
+    sc = torch.empty((n,), dtype=torch.float32, device=packed.device)
+    _check(lib.tt_fp8_dequantize(_dev_ptr(packed, "packed", (torch.uint8,)), n, k,
+                                 _dev_ptr(w, "w"), _dev_ptr(sc, "scale"), _stream(packed)))
+    return w, sc
 
 
 def normalize_device(dev):

@@ -90,6 +90,32 @@ __global__ __launch_bounds__(64) void k_i4_dequant(I4DequantArgs da) {
     }
 }
 
+struct F8DequantArgs {
+    const uint8_t *w;
+    int64_t tile_stride;
+    int32_t n, k, scale_off;
+    float *out, *scale_out;
+};
+
+// one wave per (8-row tile, 128-k unit): lane l holds 16 codes of row l % 8
+__global__ __launch_bounds__(64) void k_f8_dequant(F8DequantArgs da) {
+    const int tile = blockIdx.x, u = blockIdx.y, lane = threadIdx.x;
+    const int row = tile * kF8TileRows + (lane & 7), k0 = u * kF8UnitK + 16 * (lane >> 3);
+    if (row >= da.n) return;
+    const uint8_t *tb = da.w + (int64_t)tile * da.tile_stride;
+    if (u == 0 && lane < kF8TileRows && da.scale_out)
+        da.scale_out[row] = reinterpret_cast<const float *>(tb + da.scale_off)[lane];
+    const uint4 c = *reinterpret_cast<const uint4 *>(tb + u * kUnitBytes + lane * 16);
+    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+    for (int d = 0; d < 4; ++d) {
+        const f32x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw[d], 1.0f, false);
+        const f32x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw[d], 1.0f, true);
+        const float v[4] = {lo.x, lo.y, hi.x, hi.y};
+        for (int j = 0; j < 4; ++j)
+            if (k0 + 4 * d + j < da.k) da.out[(int64_t)row * da.k + k0 + 4 * d + j] = v[j];
+    }
+}
+
 }  // namespace tt
 
 using namespace tt;
@@ -156,6 +182,24 @@ extern "C" tt_status tt_int4_dequantize(const void *packed, int64_t n, int64_t k
     I4DequantArgs da{static_cast<const uint8_t *>(packed), g.stride, (int32_t)n, (int32_t)k,
                      (int32_t)g.units, (int32_t)g.qv_last, (int32_t)g.sz_off, w_out};
     tt_status st = launch("int4 dequantize", k_i4_dequant, grid, dim3(64), 0,
+                          static_cast<hipStream_t>(stream), da);
+    if (st == TT_OK) clear_error();
+    return st;
+}
+
+extern "C" tt_status tt_fp8_dequantize(const void *packed, int64_t n, int64_t k, float *w_out,
+                                       float *scale_out, void *stream) {
+    TT_TRY(check_ptr(packed, "packed"));
+    TT_TRY(check_ptr(w_out, "w_out"));
+    TT_TRY(check_align(packed, 16, "packed"));
+    TT_TRY(check_align(w_out, 4, "w_out"));
+    TT_TRY(check_range(n, 1, TT_MAX_ROWS, "n"));
+    TT_TRY(check_range(k, 1, TT_MAX_K_FP8, "k"));
+    const F8Geom g = f8_geom(k);
+    F8DequantArgs da{static_cast<const uint8_t *>(packed), g.stride, (int32_t)n, (int32_t)k,
+                     (int32_t)g.scale_off, w_out, scale_out};
+    tt_status st = launch("fp8 dequantize", k_f8_dequant,
+                          dim3((unsigned)ceil_div(n, kF8TileRows), (unsigned)g.units), dim3(64), 0,
                           static_cast<hipStream_t>(stream), da);
     if (st == TT_OK) clear_error();
     return st;

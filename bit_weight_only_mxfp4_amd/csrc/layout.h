@@ -26,6 +26,13 @@
 //            bytes = 4 dwords (s | z << 16) for units 4j .. 4j+3.
 //
 // Rows past N in the last tile are zero codes with scale 127 (value 0).
+//
+// FP8 E4M3 tile (row-scaled matvec; down projections have few rows and a
+// long K, so these tiles are 8 rows high to give twice as many workgroups):
+//   [codes]  units U = ceil(K / 128); one unit is 8 rows x 8 pieces x 16
+//            bytes = 1 KiB, lane l loading piece q = l / 8 (16 consecutive k)
+//            of row r = l % 8.  Codes past K and rows past N are 0.
+//   [scales] 64 bytes: 8 fp32 row scales, then 32 reserved bytes.
 #pragma once
 
 #include <stdint.h>
@@ -81,6 +88,26 @@ inline I4Geom i4_geom(int64_t k) {
     g.groups = (g.units + 3) / 4;
     g.sz_off = 256 * g.nq;
     g.stride = g.sz_off + kGroupBytes * g.groups;
+    return g;
+}
+
+constexpr int kF8TileRows = 8;
+constexpr int kF8UnitK = 128;
+constexpr int kF8TrailerBytes = 64;
+
+struct F8Geom {
+    int64_t k;
+    int64_t units;     // 128-element units per row
+    int64_t scale_off; // byte offset of the row scales
+    int64_t stride;    // bytes per tile
+};
+
+inline F8Geom f8_geom(int64_t k) {
+    F8Geom g;
+    g.k = k;
+    g.units = (k + kF8UnitK - 1) / kF8UnitK;
+    g.scale_off = 1024 * g.units;
+    g.stride = g.scale_off + kF8TrailerBytes;
     return g;
 }
 

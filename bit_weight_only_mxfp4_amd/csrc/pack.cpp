@@ -299,6 +299,48 @@ tt_status tt_quantize_int4_affine(const float *w, int64_t n, int64_t k,
     return TT_OK;
 }
 
+int64_t tt_fp8_pack_bytes(int64_t n, int64_t k) {
+    tt_status st = check_range(n, 1, TT_MAX_ROWS, "n");
+    if (st == TT_OK) st = check_range(k, 1, TT_MAX_K_FP8, "k");
+    if (st != TT_OK) return st;
+    return ceil_div(n, kF8TileRows) * f8_geom(k).stride;
+}
+
+tt_status tt_pack_fp8_matrix(const uint8_t *codes, const float *scale, int64_t n, int64_t k,
+                             void *dst, int64_t dst_bytes) {
+    TT_TRY(check_ptr(codes, "codes"));
+    TT_TRY(check_ptr(dst, "dst"));
+    int64_t need = tt_fp8_pack_bytes(n, k);
+    if (need < 0) return static_cast<tt_status>(need);
+    if (dst_bytes < need)
+        return fail(TT_E_SIZE, "dst holds %lld bytes, the pack needs %lld",
+                    (long long)dst_bytes, (long long)need);
+    const F8Geom g = f8_geom(k);
+    uint8_t *out = static_cast<uint8_t *>(dst);
+    for (int64_t t = 0; t < ceil_div(n, kF8TileRows); ++t) {
+        uint8_t *tb = out + t * g.stride;
+        // unit u, lane l = r + 8 q: 16 codes of row r at k = 128 u + 16 q ..
+        for (int64_t u = 0; u < g.units; ++u)
+            for (int l = 0; l < 64; ++l) {
+                const int64_t row = t * kF8TileRows + (l % 8);
+                const int64_t k0 = kF8UnitK * u + 16 * (l / 8);
+                uint8_t *o = tb + kUnitBytes * u + 16 * l;
+                memset(o, 0, 16);
+                if (row < n && k0 < k)
+                    memcpy(o, codes + row * k + k0, static_cast<size_t>(std::min<int64_t>(16, k - k0)));
+            }
+        float sc[kF8TileRows];
+        for (int r = 0; r < kF8TileRows; ++r) {
+            const int64_t row = t * kF8TileRows + r;
+            sc[r] = row < n ? (scale ? scale[row] : 1.0f) : 0.0f;
+        }
+        memset(tb + g.scale_off, 0, kF8TrailerBytes);
+        memcpy(tb + g.scale_off, sc, sizeof(sc));
+    }
+    clear_error();
+    return TT_OK;
+}
+
 int64_t tt_int4_pack_bytes(int64_t n, int64_t k, int64_t group) {
     tt_status st = check_range(n, 1, TT_MAX_ROWS, "n");
     if (st == TT_OK) st = check_range(k, 2, TT_MAX_K, "k");

@@ -84,6 +84,7 @@ enum { TT_SCALE_E8M0 = 0, TT_SCALE_F16 = 1 };
 #define TT_MAX_EXPERTS 256
 #define TT_MAX_TOPK 8
 #define TT_INT4_GROUP 128
+#define TT_MAX_K_FP8 32768    /* reduction dimension of the FP8 matvec */
 
 /* Library version of this header's ABI. */
 int32_t tt_abi_version(void);
@@ -265,6 +266,32 @@ tt_status tt_int4_gemv(const void *w_packed, int64_t n, int64_t k,
                        int32_t y_dtype, void *stream);
 
 /*
+ * Row-scaled FP8 matvec (kerbin.cskartikey.dev/@satvikhardat, "Dev Log #3 --
+ * SmolLM3-3B Results": the quality FP8 profile keeps gate/up and the middle
+ * down projections in FP8 and runs them as scaled matvecs -- the row's sum
+ * of weight * activation in fp32, times the row scale):
+ *   y[b][r] = scale[r] * sum_k w[r][k] * x[b][k]
+ * w is FP8 E4M3 (OCP 8-bit floating point, the E4M3 encoding: bias 7, no
+ * infinities, S.1111.111 = NaN; the pages say "FP8" only).  In this library
+ * it serves the dense down projection after the gate/up SwiGLU (x = its
+ * output h, fp32 or bf16).
+ *
+ * tt_fp8_pack_bytes / tt_pack_fp8_matrix: canonical codes u8[n][k] and
+ * scale f32[n] (NULL = ones) -> the private tiled layout (8-row tiles;
+ * host buffers).
+ * tt_fp8_gemv: w_packed from tt_pack_fp8_matrix (device); x [batch][k] of
+ * x_dtype (TT_F32 or TT_BF16), 16-byte aligned, k a multiple of 8 (bf16) or
+ * 4 (fp32), k <= TT_MAX_K_FP8; y [batch][n] of y_dtype.  Products and sums
+ * in fp32, the row scale applied to the full sum.
+ */
+int64_t tt_fp8_pack_bytes(int64_t n, int64_t k);
+tt_status tt_pack_fp8_matrix(const uint8_t *codes, const float *scale,
+                             int64_t n, int64_t k, void *dst, int64_t dst_bytes);
+tt_status tt_fp8_gemv(const void *w_packed, int64_t n, int64_t k, const void *x,
+                      int32_t x_dtype, int64_t batch, void *y, int32_t y_dtype,
+                      void *stream);
+
+/*
  * Decoded weights, for checking the packed layouts bit for bit: w[r][k] =
  * E2M1(code) * 2^(e-127) rounded once to fp32 (NaN for e = 0xFF).
  * tt_mxfp4_dequantize takes a tt_pack_mxfp4_matrix pack (w_out [n][k],
@@ -280,6 +307,10 @@ tt_status tt_mxfp4_gateup_dequantize(const void *packed, int64_t inter,
                                      void *stream);
 tt_status tt_int4_dequantize(const void *packed, int64_t n, int64_t k,
                              int64_t group, float *w_out, void *stream);
+/* FP8: w_out [n][k] = E4M3(code) in fp32 (NaN for S.1111.111), scale_out
+ * [n] or NULL. */
+tt_status tt_fp8_dequantize(const void *packed, int64_t n, int64_t k,
+                            float *w_out, float *scale_out, void *stream);
 
 #ifdef __cplusplus
 }

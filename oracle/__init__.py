@@ -229,7 +229,12 @@ def fp8_gemv(w, scale, n, k, x, rows=None):
     w = _c(w, np.uint8)
     scale = _c(scale, np.float32)
     x = np.asarray(x)
-    x_f32 = 1 if x.dtype == np.float32 else 0
+    if x.dtype.kind == "f":
+        x_f32 = 1
+    elif x.dtype in (np.uint16, np.int16):
+        x_f32 = 0
+    else:
+        raise TypeError("x must be floating point (fp32 values) or bf16 bit patterns")
     x = _c(x, np.float32 if x_f32 else np.uint16).reshape(-1, k)
     batch = x.shape[0]
     r = None if rows is None else _c(rows, np.int64)

@@ -224,3 +224,40 @@ def test_mxfp4_quantizer_errors_write_nothing():
     rc = tt.lib.tt_quantize_mxfp4(w.ctypes.data, 2, 48, codes.ctypes.data, scales.ctypes.data,
                                   None)
     assert rc == -2
+
+
+@pytest.mark.parametrize("n,k", [(13, 200), (8, 128), (20, 300)])
+def test_fp8_pack_follows_documented_layout(n, k):
+    codes, scale = workloads.fp8_matrix(5, 0, n, k)
+    packed = tt.pack_fp8_matrix(codes, scale, n, k)
+    units = -(-k // 128)
+    stride = 1024 * units + 64
+    tiles = -(-n // 8)
+    assert packed.size == tiles * stride == tt.fp8_pack_bytes(n, k)
+    for t in range(tiles):
+        tb = packed[t * stride:(t + 1) * stride]
+        sc = tb[1024 * units:1024 * units + 32].view(np.float32)
+        for r in range(8):
+            row = 8 * t + r
+            assert sc[r] == (scale[row] if row < n else 0.0)
+            for u in range(units):
+                for q in range(8):
+                    got = tb[1024 * u + 16 * (r + 8 * q):][:16]
+                    k0 = 128 * u + 16 * q
+                    want = np.zeros(16, np.uint8)
+                    if row < n and k0 < k:
+                        seg = codes[row, k0:min(k0 + 16, k)]
+                        want[:seg.size] = seg
+                    assert np.array_equal(got, want), (t, r, u, q)
+
+
+def test_fp8_validation():
+    P = ctypes.c_void_p(16)
+    assert tt.lib.tt_fp8_gemv(P, 8, 100, P, 1, 1, P, 0, None) == -2   # bf16 needs k % 8
+    assert tt.lib.tt_fp8_gemv(P, 8, 102, P, 0, 1, P, 0, None) == -2   # fp32 needs k % 4
+    assert tt.lib.tt_fp8_gemv(None, 8, 128, P, 0, 1, P, 0, None) == -1
+    assert tt.lib.tt_fp8_gemv(P, 8, 128, P, 2, 1, P, 0, None) == -4   # dtype
+    assert tt.lib.tt_fp8_gemv(P, 8, 40000, P, 0, 1, P, 0, None) == -2  # k range
+    assert tt.lib.tt_fp8_gemv(P, 8, 128, P, 0, 33, P, 0, None) == -2   # batch range
+    assert tt.lib.tt_fp8_gemv(ctypes.c_void_p(8), 8, 128, P, 0, 1, P, 0, None) == -3
+    assert tt.fp8_pack_bytes(16, 256) == 2 * (2 * 1024 + 64)

@@ -29,6 +29,7 @@ import numpy as np
 
 # tensor ids in the seed sequence
 T_X, T_GC, T_GE, T_GP, T_UC, T_UE, T_UP, T_DC, T_DE, T_DP, T_LOGITS, T_INT4W, T_OX = range(13)
+T_F8C, T_F8S, T_H = 13, 14, 15
 
 E8M0_LO, E8M0_HI = 119, 125          # 2^-8 .. 2^-2 inclusive
 
@@ -124,6 +125,24 @@ def int4_source(wid: int, layer: int, n: int, k: int, tensor: int = T_INT4W,
                 seed: int = 0) -> np.ndarray:
     return (0.02 * rng(wid, layer, tensor, seed=seed).standard_normal(
         (n, k), dtype=np.float32)).astype(np.float32)
+
+
+def fp8_matrix(wid: int, layer: int, n: int, k: int, seed: int = 0):
+    """FP8 E4M3 codes u8[n][k] drawn uniformly over the finite codes (the
+    two NaN patterns are excluded) and row scales U(0.5, 1.5) / 448."""
+    c = rng(wid, layer, T_F8C, seed=seed).integers(0, 254, (n, k), dtype=np.int64)
+    c = np.where(c >= 0x7F, c + 1, c).astype(np.uint8)   # skip 0x7F; 0xFF is above
+    s = (rng(wid, layer, T_F8S, seed=seed).uniform(0.5, 1.5, n) / 448.0).astype(np.float32)
+    return c, s
+
+
+def swiglu_like(wid: int, layer: int, batch: int, k: int, seed: int = 0) -> np.ndarray:
+    """fp32 activations shaped like a gate/up SwiGLU output: silu(a) * b for
+    a, b ~ N(0, 1)."""
+    g = rng(wid, layer, T_H, seed=seed)
+    a = g.standard_normal((batch, k))
+    b = g.standard_normal((batch, k))
+    return (a / (1.0 + np.exp(-a)) * b).astype(np.float32)
 
 
 def attention_shapes(w: Workload):
