@@ -70,6 +70,7 @@ def lib() -> ctypes.CDLL:
                                            I64, P, I64, P, P]),
             "or_mxfp4_quantize": (ctypes.c_int, [P, I64, I64, P, P, P]),
             "or_fp8e4m3_value": (D, [ctypes.c_int]),
+            "or_gqa_attention": (None, [P, P, P, I64, I64, I64, I64, I64, D, P, P, P]),
             "or_fp8_gemv": (None, [P, P, I64, I64, P, ctypes.c_int, I64, P, I64, P, P]),
             "or_int4_quantize": (ctypes.c_int, [P, I64, I64, I64, P, P, P]),
             "or_int4_dequantize": (None, [P, P, P, I64, I64, I64, P]),
@@ -217,6 +218,19 @@ def moe_down_combine(d_bank, n_exp, hidden, inter, h, ids, w, rows=None):
 
 
 # ---- INT4 ---------------------------------------------------------------
+
+def gqa_attention(q, K, V, hq, hkv, d, tcap, T, scale):
+    """Single-token GQA attention (bf16 bit patterns q [hq][d], K and V
+    [hkv][tcap][d]).  Returns (out, A, Smax) in fp64: out [hq][d], A =
+    sum_t p_t |V| [hq][d], Smax = max_t scale * sum |K q| [hq]."""
+    q, K, V = _c(q, np.uint16), _c(K, np.uint16), _c(V, np.uint16)
+    out = np.empty((hq, d), np.float64)
+    A = np.empty((hq, d), np.float64)
+    Sm = np.empty(hq, np.float64)
+    lib().or_gqa_attention(_p(q), _p(K), _p(V), hq, hkv, d, tcap, T, float(scale), _p(out),
+                           _p(A), _p(Sm))
+    return out, A, Sm
+
 
 def fp8e4m3_value(code):
     return lib().or_fp8e4m3_value(int(code))

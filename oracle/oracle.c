@@ -444,6 +444,69 @@ void or_fp8_gemv(const uint8_t *w, const float *scale, int64_t n, int64_t k,
 }
 
 /* ------------------------------------------------------------------ */
+/* Single-token GQA attention                                          */
+/* ------------------------------------------------------------------ */
+
+/*
+ * Single-token grouped-query attention over a bf16 KV cache ([DL3]: each
+ * query head h reads kv head h / (hq / hkv); a score is the key . query dot
+ * product times the scale; the attention output is the softmax-weighted sum
+ * of the values over the T cached positions):
+ *   s_t     = scale * sum_d K[g][t][d] q[h][d],    g = h / (hq / hkv)
+ *   p_t     = exp(s_t - max_u s_u) / sum_u exp(s_u - max_u s_u)
+ *   o[h][d] = sum_t p_t V[g][t][d]
+ * q: bf16 [hq][d]; K, V: bf16, row t of kv head g at ((g * tcap) + t) * d;
+ * everything in fp64.  out [hq][d]; A (NULL allowed) [hq][d] =
+ * sum_t p_t |V[g][t][d]|; Smax (NULL allowed) [hq] = max_t scale *
+ * sum_d |K q| (the error scales of the output and of the scores).
+ */
+void or_gqa_attention(const uint16_t *q, const uint16_t *K, const uint16_t *V,
+                      int64_t hq, int64_t hkv, int64_t d, int64_t tcap,
+                      int64_t T, double scale, double *out, double *A,
+                      double *Smax)
+{
+    double *s = (double *)malloc((size_t)T * sizeof(double));
+    double *mag = (double *)malloc((size_t)T * sizeof(double));
+    for (int64_t h = 0; h < hq; ++h) {
+        int64_t g = h / (hq / hkv);
+        double m = -INFINITY, den = 0.0, smax = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            const uint16_t *kr = K + (g * tcap + t) * d;
+            double acc = 0.0, a = 0.0;
+            for (int64_t j = 0; j < d; ++j) {
+                double pr = or_bf16_value(kr[j]) * or_bf16_value(q[h * d + j]);
+                acc += pr;
+                a += fabs(pr);
+            }
+            s[t] = scale * acc;
+            mag[t] = fabs(scale) * a;
+            if (s[t] > m)
+                m = s[t];
+            if (mag[t] > smax)
+                smax = mag[t];
+        }
+        for (int64_t t = 0; t < T; ++t)
+            den += exp(s[t] - m);
+        for (int64_t j = 0; j < d; ++j) {
+            double acc = 0.0, a = 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                double p = exp(s[t] - m) / den;
+                double v = or_bf16_value(V[(g * tcap + t) * d + j]);
+                acc += p * v;
+                a += p * fabs(v);
+            }
+            out[h * d + j] = acc;
+            if (A)
+                A[h * d + j] = a;
+        }
+        if (Smax)
+            Smax[h] = smax;
+    }
+    free(s);
+    free(mag);
+}
+
+/* ------------------------------------------------------------------ */
 /* MXFP4 quantizer                                                     */
 /* ------------------------------------------------------------------ */
 
