@@ -16,8 +16,8 @@ host (a reported baseline, not a target).
 
 Other workloads (--workload): tiny, phi4 (gate/up), phi4-int4 (QKV + O),
 gptoss (routing fused into the expert gate/up, then down/combine), batched
-(--batch B), fp8-down (row-scaled FP8 down projection), quantize (host MXFP4
-quantizer).
+(--batch B), fp8-down (row-scaled FP8 down projection), attention
+(single-token GQA attention, --context T), quantize (host MXFP4 quantizer).
 """
 from __future__ import annotations
 
@@ -324,6 +324,46 @@ def run(args):
                                     peak=PEAK_HBM_GBS, unit="GB/s",
                                     frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
 
+    elif args.workload == "attention":
+        # single-token GQA attention, Phi-4-shaped heads (40 query / 10 kv x
+        # 128), a 4096-position bf16 KV cache per layer, 24 layers rotated
+        hq, hkv, d, T, layers = 40, 10, 128, args.context, 24
+        log(f"setup attention hq {hq} hkv {hkv} d {d} T {T}, {layers} layers")
+        gen = np.random.default_rng([0, 77])
+        caches = []
+        for layer in range(2):
+            kc = workloads.bf16_bits(gen.standard_normal((hkv, T, d)).astype(np.float32))
+            vc = workloads.bf16_bits(gen.standard_normal((hkv, T, d)).astype(np.float32))
+            caches.append((torch.from_numpy(kc.view(np.int16)).to(dev),
+                           torch.from_numpy(vc.view(np.int16)).to(dev)))
+        while len(caches) < layers:
+            caches.append(tuple(c.clone() for c in caches[len(caches) % 2]))
+        q = torch.from_numpy(workloads.bf16_bits(gen.standard_normal((hq, d)).astype(np.float32))
+                             .view(np.int16)).to(dev)
+        out = torch.empty((hq, d), dtype=torch.float32, device=dev)
+        ws = torch.empty(tt.gqa_attention_workspace_bytes(hq, hkv, d, T), dtype=torch.uint8,
+                         device=dev)
+        scale = 1.0 / np.sqrt(d)
+
+        def step():
+            for kc_, vc_ in caches:
+                tt.gqa_attention_decode(q, kc_, vc_, hq, hkv, d, T, scale, out=out, workspace=ws)
+
+        secs = time_graph(torch, capture(torch, step), K, W)
+        calls = K * layers
+        per_call = 2 * hkv * T * d * 2 + hq * d * 2 + hq * d * 4
+        gbs = per_call * calls / secs / 1e9
+        result = dict(metric="effective HBM GB/s of single-token GQA attention over a bf16 KV "
+                             "cache",
+                      value=round(gbs, 2), unit="GB/s", us_per_call=round(secs / calls * 1e6, 3),
+                      ms_per_step=round(secs / K * 1e3, 4), bytes_per_call=per_call,
+                      config=dict(workload=f"phi4-14b-gqa-attention-40-10x128-T{T}", hq=hq,
+                                  hkv=hkv, d=d, T=T, layers_rotated=layers,
+                                  launch="one HIP graph per step (2 kernels per call)"),
+                      roofline=dict(bound="hbm", kernel="k_attn_partial+k_attn_combine",
+                                    achieved=round(gbs, 2), peak=PEAK_HBM_GBS, unit="GB/s",
+                                    frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
+
     elif args.workload == "quantize":
         # host-side MXFP4 quantizer + postscale fit on one SmolLM3-shaped
         # layer's fp32 gate and up rows (a host function: no GPU work)
@@ -357,6 +397,7 @@ def run(args):
         raise SystemExit(f"unknown workload {args.workload}")
 
     dtype = {"phi4-int4": "int4 x bf16 -> fp32 accumulate",
+             "attention": "bf16 x bf16 -> fp32 accumulate",
              "fp8-down": "fp8-e4m3 x fp32 -> fp32 accumulate",
              "quantize": "fp32 -> fp4-e2m1 + e8m0 (host)"}.get(
                  args.workload, "fp4-e2m1 x bf16 -> fp32 accumulate")
@@ -394,8 +435,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="smollm3",
                     choices=["smollm3", "tiny", "phi4", "phi4-int4", "gptoss", "batched",
-                             "fp8-down", "quantize"])
+                             "fp8-down", "attention", "quantize"])
     ap.add_argument("--batch", type=int, default=8)
+    ap.add_argument("--context", type=int, default=4096,
+                    help="cached positions for --workload attention")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",

@@ -56,6 +56,9 @@ _SIGS = {
                                          _I64, _P, _I32, _P]),
     "tt_int4_gemv": (_I32, [_P, _I64, _I64, _I64, _P, _I64, _P, _I32, _P]),
     "tt_fp8_gemv": (_I32, [_P, _I64, _I64, _P, _I32, _I64, _P, _I32, _P]),
+    "tt_gqa_attention_workspace_bytes": (_I64, [_I64, _I64, _I64, _I64]),
+    "tt_gqa_attention_decode": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64,
+                                        ctypes.c_float, _P, _I32, _P, _I64, _P]),
     "tt_mxfp4_dequantize": (_I32, [_P, _I64, _I64, _P, _P, _P]),
     "tt_mxfp4_gateup_dequantize": (_I32, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
     "tt_int4_dequantize": (_I32, [_P, _I64, _I64, _I64, _P, _P]),
@@ -339,6 +342,31 @@ def fp8_gemv(w_packed, n, k, x, out=None, out_dtype=None):
     _check(lib.tt_fp8_gemv(_dev_ptr(w_packed, "w_packed", (torch.uint8,)), n, k,
                            _dev_ptr(x, "x"), _dtype_code(x.dtype), batch, _dev_ptr(out, "y"),
                            _dtype_code(out.dtype), _stream(x)))
+    return out
+
+
+def gqa_attention_workspace_bytes(hq, hkv, d, T) -> int:
+    return _size(lib.tt_gqa_attention_workspace_bytes(hq, hkv, d, T))
+
+
+def gqa_attention_decode(q, k_cache, v_cache, hq, hkv, d, T, scale, out=None, out_dtype=None,
+                         workspace=None):
+    """Single-token GQA attention: q bf16 [hq][d], k_cache / v_cache bf16
+    [hkv][tcap][d] (positions 0..T-1 attended).  ``workspace`` (uint8 device
+    tensor) is allocated here when not given."""
+    torch = _torch()
+    for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _acts(t, name)
+    tcap = k_cache.numel() // (hkv * d)
+    if out is None:
+        out = torch.empty((hq, d), dtype=out_dtype or torch.float32, device=q.device)
+    need = gqa_attention_workspace_bytes(hq, hkv, d, T)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib.tt_gqa_attention_decode(
+        _dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"), hq, hkv,
+        d, tcap, T, float(scale), _dev_ptr(out, "out"), _dtype_code(out.dtype),
+        _dev_ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(q)))
     return out
 
 

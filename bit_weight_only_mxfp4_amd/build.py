@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libtt.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["abi.cpp", "pack.cpp", "mxfp4_gateup.hip", "int4_gemv.hip", "moe.hip", "fp8_gemv.hip",
+SOURCES = ["abi.cpp", "pack.cpp", "mxfp4_gateup.hip", "int4_gemv.hip", "moe.hip", "fp8_gemv.hip", "attention.hip",
            "dequant.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -85,6 +85,7 @@ enum { TT_SCALE_E8M0 = 0, TT_SCALE_F16 = 1 };
 #define TT_MAX_TOPK 8
 #define TT_INT4_GROUP 128
 #define TT_MAX_K_FP8 32768    /* reduction dimension of the FP8 matvec */
+#define TT_MAX_ATTN_T (1 << 20) /* cached positions of one attention call */
 
 /* Library version of this header's ABI. */
 int32_t tt_abi_version(void);
@@ -290,6 +291,28 @@ tt_status tt_pack_fp8_matrix(const uint8_t *codes, const float *scale,
 tt_status tt_fp8_gemv(const void *w_packed, int64_t n, int64_t k, const void *x,
                       int32_t x_dtype, int64_t batch, void *y, int32_t y_dtype,
                       void *stream);
+
+/*
+ * Single-token grouped-query attention over a bf16 KV cache
+ * (kerbin.cskartikey.dev/@satvikhardat, "Dev Log #3 -- SmolLM3-3B Results":
+ * each query head h reads kv head g = h / (hq / hkv); scores are key . query
+ * times the scale; the output is the softmax-weighted sum of the values):
+ *   s_t     = scale * sum_d K[g][t][d] q[h][d],  t = 0 .. T-1
+ *   out[h]  = sum_t softmax(s)_t V[g][t]
+ * q: bf16 [hq][d]; k_cache, v_cache: bf16, row t of kv head g at element
+ * ((g * tcap) + t) * d, T <= tcap (all device memory, 16-byte aligned);
+ * d is 64 or 128; hq / hkv is 1, 2, 4 or 8; out [hq][d] of out_dtype.
+ * workspace: device memory of at least tt_gqa_attention_workspace_bytes
+ * bytes for the per-chunk partial results (64 positions per chunk); it
+ * needs no initialisation, its contents are overwritten, and calls that
+ * share one workspace must not overlap.  Scores, exponentials and sums in
+ * fp32; the chunks are combined in a fixed order.  Two kernel launches.
+ */
+int64_t tt_gqa_attention_workspace_bytes(int64_t hq, int64_t hkv, int64_t d, int64_t T);
+tt_status tt_gqa_attention_decode(const void *q, const void *k_cache, const void *v_cache,
+                                  int64_t hq, int64_t hkv, int64_t d, int64_t tcap,
+                                  int64_t T, float scale, void *out, int32_t out_dtype,
+                                  void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * Decoded weights, for checking the packed layouts bit for bit: w[r][k] =

@@ -261,3 +261,21 @@ def test_fp8_validation():
     assert tt.lib.tt_fp8_gemv(P, 8, 128, P, 0, 33, P, 0, None) == -2   # batch range
     assert tt.lib.tt_fp8_gemv(ctypes.c_void_p(8), 8, 128, P, 0, 1, P, 0, None) == -3
     assert tt.fp8_pack_bytes(16, 256) == 2 * (2 * 1024 + 64)
+
+
+def test_attention_validation():
+    P = ctypes.c_void_p(16)
+    f = tt.lib.tt_gqa_attention_decode
+    ok = dict(hq=40, hkv=10, d=128, tcap=512, T=300)
+    need = tt.gqa_attention_workspace_bytes(40, 10, 128, 300)
+    assert need == 40 * 5 * 130 * 4
+    def call(hq=40, hkv=10, d=128, tcap=512, T=300, ws=need, dt=0, ptr=P):
+        return f(ptr, P, P, hq, hkv, d, tcap, T, 0.1, P, dt, P, ws, None)
+    assert call(hq=30) == -2              # not a multiple
+    assert call(hq=48, hkv=4) == -2       # group 12
+    assert call(d=96) == -2
+    assert call(T=600) == -2              # T > tcap
+    assert call(ws=need - 1) == -5
+    assert call(dt=3) == -4
+    assert call(ptr=None) == -1
+    assert call(ptr=ctypes.c_void_p(8)) == -3
