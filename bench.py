@@ -17,7 +17,8 @@ host (a reported baseline, not a target).
 Other workloads (--workload): tiny, phi4 (gate/up), phi4-int4 (QKV + O),
 gptoss (routing fused into the expert gate/up, then down/combine), batched
 (--batch B), fp8-down (row-scaled FP8 down projection), attention
-(single-token GQA attention, --context T), quantize (host MXFP4 quantizer).
+(single-token GQA attention, --context T), phi4-layer (a whole dense decode
+layer as one graph), quantize (host MXFP4 quantizer).
 """
 from __future__ import annotations
 
@@ -364,6 +365,72 @@ def run(args):
                                     achieved=round(gbs, 2), peak=PEAK_HBM_GBS, unit="GB/s",
                                     frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
 
+    elif args.workload == "phi4-layer":
+        # one dense decode layer as one HIP graph, Phi-4 shapes: INT4 QKV ->
+        # GQA attention (bf16 KV cache, --context positions) -> INT4 O ->
+        # MXFP4 gate/up SwiGLU -> FP8 down; 8 layers rotated
+        w = workloads.PHI4
+        hq, hkv, d = w.heads
+        T, layers, distinct = args.context, 8, 2
+        (nq, kq), (no, ko) = workloads.attention_shapes(w)
+        log(f"setup Phi-4-shaped decode layer, T {T}, {layers} layers ({distinct} generated)")
+        gen = np.random.default_rng([0, 78])
+        L = []
+        for layer in range(distinct):
+            qkv = tt.pack_int4(*tt.quantize_int4_affine(
+                workloads.int4_source(w.wid, layer, nq, kq)), nq, kq)
+            o4 = tt.pack_int4(*tt.quantize_int4_affine(
+                workloads.int4_source(w.wid, layer, no, ko, workloads.T_INT4W + 100)), no, ko)
+            gu = tt.pack_mxfp4_gateup(*workloads.gateup(w, layer), w.inter, w.hidden)
+            dc, dsc = workloads.fp8_matrix(w.wid, layer, w.hidden, w.inter)
+            dn = tt.pack_fp8_matrix(dc, dsc, w.hidden, w.inter)
+            kc = workloads.bf16_bits(gen.standard_normal((hkv, T, d)).astype(np.float32))
+            vc = workloads.bf16_bits(gen.standard_normal((hkv, T, d)).astype(np.float32))
+            L.append([torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+                      for a in (qkv, o4, gu, dn, kc, vc)])
+        while len(L) < layers:
+            L.append([t.clone() for t in L[len(L) % distinct]])
+        x = torch.from_numpy(workloads.activations(w.wid, 0, 1, w.hidden).view(np.int16)).to(dev)
+        ws = torch.empty(tt.gqa_attention_workspace_bytes(hq, hkv, d, T), dtype=torch.uint8,
+                         device=dev)
+        bf = torch.bfloat16
+        yq = torch.empty((1, nq), dtype=bf, device=dev)
+        att = torch.empty((hq, d), dtype=bf, device=dev)
+        yo = torch.empty((1, no), dtype=bf, device=dev)
+        h = torch.empty((1, w.inter), device=dev)
+        y = torch.empty((1, w.hidden), device=dev)
+
+        def layer_calls(qkv, o4, gu, dn, kc, vc):
+            tt.int4_gemv(qkv, nq, kq, x, out=yq)
+            tt.gqa_attention_decode(yq[0, :hq * d], kc.view(bf), vc.view(bf), hq, hkv, d, T,
+                                    d ** -0.5, out=att, workspace=ws)
+            tt.int4_gemv(o4, no, ko, att.view(1, hq * d), out=yo)
+            tt.mxfp4_gateup_swiglu(gu, w.inter, w.hidden, yo, out=h)
+            tt.fp8_gemv(dn, w.hidden, w.inter, h, out=y)
+
+        graphs = [capture(torch, lambda l=l: layer_calls(*l)) for l in L]
+
+        def step():
+            for g in graphs:
+                g.replay()
+
+        secs = time_steps(torch, step, K, W)
+        per_layer = (int4_bytes(nq, kq, 1) - nq * 2 + 2 * hkv * T * d * 2 + hq * d * 2
+                     + int4_bytes(no, ko, 1) - no * 2 + gateup_bytes(w.inter, w.hidden, 1)
+                     + w.hidden * w.inter + w.hidden * 4 + w.inter * 4 + w.hidden * 4)
+        gbs = per_layer * layers * K / secs / 1e9
+        result = dict(metric="effective HBM GB/s of one dense decode layer run as one HIP graph "
+                             "(INT4 QKV, GQA attention, INT4 O, MXFP4 gate/up SwiGLU, FP8 down)",
+                      value=round(gbs, 2), unit="GB/s",
+                      us_per_layer=round(secs / (K * layers) * 1e6, 3),
+                      ms_per_step=round(secs / K * 1e3, 4), bytes_per_layer=per_layer,
+                      config=dict(workload=f"phi4-14b-decode-layer-T{T}", hidden=w.hidden,
+                                  inter=w.inter, heads=[hq, hkv, d], T=T, layers_rotated=layers,
+                                  launch="one HIP graph per layer (6 kernels)"),
+                      roofline=dict(bound="hbm", kernel="layer graph", achieved=round(gbs, 2),
+                                    peak=PEAK_HBM_GBS, unit="GB/s",
+                                    frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
+
     elif args.workload == "quantize":
         # host-side MXFP4 quantizer + postscale fit on one SmolLM3-shaped
         # layer's fp32 gate and up rows (a host function: no GPU work)
@@ -397,6 +464,7 @@ def run(args):
         raise SystemExit(f"unknown workload {args.workload}")
 
     dtype = {"phi4-int4": "int4 x bf16 -> fp32 accumulate",
+             "phi4-layer": "int4 / fp4-e2m1 / fp8-e4m3 / bf16 x bf16 -> fp32 accumulate",
              "attention": "bf16 x bf16 -> fp32 accumulate",
              "fp8-down": "fp8-e4m3 x fp32 -> fp32 accumulate",
              "quantize": "fp32 -> fp4-e2m1 + e8m0 (host)"}.get(
@@ -435,7 +503,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="smollm3",
                     choices=["smollm3", "tiny", "phi4", "phi4-int4", "gptoss", "batched",
-                             "fp8-down", "attention", "quantize"])
+                             "fp8-down", "attention", "phi4-layer", "quantize"])
     ap.add_argument("--batch", type=int, default=8)
     ap.add_argument("--context", type=int, default=4096,
                     help="cached positions for --workload attention")

@@ -81,3 +81,55 @@ def test_graph_replays_match_eager(dev):
         torch.cuda.synchronize()
         for k in outs:
             assert torch.equal(outs[k], eager[k]), (rep, k)
+
+
+def test_one_graph_per_dense_decode_layer(dev):
+    """A whole dense decode layer captured as one graph -- INT4 QKV (bf16
+    out) -> GQA attention on the q heads -> INT4 O (bf16 out) -> MXFP4
+    gate/up SwiGLU -> FP8 down -- every replay equal to the eager chain."""
+    hq, hkv, d, T, hidden, inter = 8, 2, 128, 300, 1024, 768
+    nq = (hq + 2 * hkv) * d
+    gen = np.random.default_rng(5)
+    qkv = dev_u8(tt.pack_int4(*tt.quantize_int4_affine(
+        workloads.int4_source(3, 0, nq, hidden)), nq, hidden), dev)
+    o4 = dev_u8(tt.pack_int4(*tt.quantize_int4_affine(
+        workloads.int4_source(3, 1, hidden, hq * d)), hidden, hq * d), dev)
+    w = workloads.Workload(3, "layer", hidden, inter)
+    gu = dev_u8(tt.pack_mxfp4_gateup(*workloads.gateup(w), inter, hidden), dev)
+    dc, dsc = workloads.fp8_matrix(3, 0, hidden, inter)
+    dn = dev_u8(tt.pack_fp8_matrix(dc, dsc, hidden, inter), dev)
+    kc = dev_bf16(workloads.bf16_bits(gen.standard_normal((hkv, T, d)).astype(np.float32)), dev)
+    vc = dev_bf16(workloads.bf16_bits(gen.standard_normal((hkv, T, d)).astype(np.float32)), dev)
+    x = dev_bf16(workloads.activations(3, 0, 1, hidden), dev)
+    ws = torch.empty(tt.gqa_attention_workspace_bytes(hq, hkv, d, T), dtype=torch.uint8,
+                     device=dev)
+    outs = dict(qkv=torch.empty((1, nq), dtype=torch.bfloat16, device=dev),
+                att=torch.empty((hq, d), dtype=torch.bfloat16, device=dev),
+                o=torch.empty((1, hidden), dtype=torch.bfloat16, device=dev),
+                h=torch.empty((1, inter), device=dev),
+                y=torch.empty((1, hidden), device=dev))
+
+    def step():
+        tt.int4_gemv(qkv, nq, hidden, x, out=outs["qkv"])
+        q = outs["qkv"][0, :hq * d]
+        tt.gqa_attention_decode(q, kc, vc, hq, hkv, d, T, d ** -0.5, out=outs["att"],
+                                workspace=ws)
+        tt.int4_gemv(o4, hidden, hq * d, outs["att"].view(1, hq * d), out=outs["o"])
+        tt.mxfp4_gateup_swiglu(gu, inter, hidden, outs["o"], out=outs["h"])
+        tt.fp8_gemv(dn, hidden, inter, outs["h"], out=outs["y"])
+
+    graph = _capture(step)
+    for rep in range(3):
+        x.copy_(dev_bf16(workloads.bf16_bits(gen.standard_normal((1, hidden))
+                                             .astype(np.float32)), dev))
+        torch.cuda.synchronize()
+        step()
+        torch.cuda.synchronize()
+        eager = {k: v.clone() for k, v in outs.items()}
+        for v in outs.values():
+            v.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in outs:
+            assert torch.equal(outs[k], eager[k]), (rep, k)
+        assert torch.isfinite(outs["y"]).all()
