@@ -323,7 +323,10 @@ def run(args):
                                   launch="one HIP graph per step"),
                       roofline=dict(bound="hbm", kernel="k_fp8_gemv", achieved=round(gbs, 2),
                                     peak=PEAK_HBM_GBS, unit="GB/s",
-                                    frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
+                                    frac=round(gbs / PEAK_HBM_GBS, 4),
+                                    traffic=profiled_traffic(
+                                        ("fp8_gemv.hip", "device.h", "layout.h"),
+                                        "fp8_down_smollm3.md")))
 
     elif args.workload == "attention":
         # single-token GQA attention, Phi-4-shaped heads (40 query / 10 kv x
@@ -363,7 +366,10 @@ def run(args):
                                   launch="one HIP graph per step (2 kernels per call)"),
                       roofline=dict(bound="hbm", kernel="k_attn_partial+k_attn_combine",
                                     achieved=round(gbs, 2), peak=PEAK_HBM_GBS, unit="GB/s",
-                                    frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
+                                    frac=round(gbs / PEAK_HBM_GBS, 4),
+                                    traffic=profiled_traffic(
+                                        ("attention.hip", "device.h"),
+                                        "attention_phi4_t4096.md") if T == 4096 else None))
 
     elif args.workload == "phi4-layer":
         # one dense decode layer as one HIP graph, Phi-4 shapes: INT4 QKV ->
