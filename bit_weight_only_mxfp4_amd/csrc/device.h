@@ -92,6 +92,31 @@ __device__ __forceinline__ bf16x8_t fp4x8_to_bf16x8(uint32_t c, float sc) {
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// Cross-lane sums over lane pairs (l, l ^ 8), (l, l ^ 16), (l, l ^ 32) without
+// LDS permutes: a DPP rotate by 8 within each row of 16 lanes, and the gfx950
+// row-swap instructions (v_permlane16_swap / v_permlane32_swap exchange odd
+// rows with even rows, resp. the upper half-wave with the lower).  Both lanes
+// of a pair get the same bits.  All 64 lanes must be active.
+__device__ __forceinline__ float sum_xor8(float v) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                             0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF,
+                                             false));
+}
+// (The pair of results is bit-cast as a whole vector: a bit_cast of one
+// element of an ext-vector value is miscompiled to element 0.)
+__device__ __forceinline__ float sum_xor16(float v) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, v);
+    const f32x2_t r =
+        __builtin_bit_cast(f32x2_t, __builtin_amdgcn_permlane16_swap(b, b, false, false));
+    return r.x + r.y;
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, v);
+    const f32x2_t r =
+        __builtin_bit_cast(f32x2_t, __builtin_amdgcn_permlane32_swap(b, b, false, false));
+    return r.x + r.y;
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {

@@ -143,9 +143,7 @@ __global__ __launch_bounds__(1024) void k_fp8_gemv(F8Args a) {
     // the 8 pieces of each row -> row partial in lanes r (0..7)
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        acc[t] += __shfl_xor(acc[t], 8);
-        acc[t] += __shfl_xor(acc[t], 16);
-        acc[t] += __shfl_xor(acc[t], 32);
+        acc[t] = sum_xor32(sum_xor16(sum_xor8(acc[t])));
     }
     if (ks > 1) {
         if (lane < kF8TileRows)

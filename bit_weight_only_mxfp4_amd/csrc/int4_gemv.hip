@@ -199,8 +199,7 @@ __global__ __launch_bounds__(1024) void k_int4_gemv(I4Args a) {
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        acc[t] += __shfl_xor(acc[t], 16);
-        acc[t] += __shfl_xor(acc[t], 32);
+        acc[t] = sum_xor32(sum_xor16(acc[t]));
     }
     if (ks > 1) {
         if (lane < 16)

@@ -208,8 +208,7 @@ __global__ __launch_bounds__(1024) void k_down_combine(DownArgs a) {
                 acc = fmaf(fp4x32_dot_bf16(c[i], xb + i * 16),
                            e8m0_f32((sd[i >> 2] >> (8 * (i & 3))) & 255u), acc);
         }
-        acc += __shfl_xor(acc, 16);
-        acc += __shfl_xor(acc, 32);
+        acc = sum_xor32(sum_xor16(acc));
         if (slot_ok) {
             if (lane < 16) red[(j * S + part) * 16 + lane] = acc;
             if (part == 0 && lane < 16) pss[j * 17 + lane] = ps;

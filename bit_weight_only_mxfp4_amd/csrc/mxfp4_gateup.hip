@@ -57,6 +57,21 @@ __device__ __forceinline__ uint32_t gu_route_key(uint32_t bits, int e) {
     return (ord << 16) | (0xFFFFu - (uint32_t)e);
 }
 
+// Maximum over the wave: DPP steps within each row of 16 lanes (quad swaps,
+// then the half-row and row mirrors), then the four row maxima read out as
+// scalars.  No LDS permutes.
+__device__ __forceinline__ uint32_t gu_wave_max(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(r0, r1), max(r2, r3));
+}
+
 // Expert of slot j for one token, by iterated wave maxima over the keys of
 // the token's logits (4 per lane; keys past the expert count are 0, below
 // every real key).  A key carries both its logit and its expert index, so
@@ -72,10 +87,7 @@ __device__ __forceinline__ int gu_route_topj(uint32_t key[4], int topk, int j, b
     for (int r = 0; r < TT_MAX_TOPK; ++r) {
         sel[r] = 0.0f;
         if (r < need) {
-            uint32_t m = max(max(key[0], key[1]), max(key[2], key[3]));
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1)
-                m = max(m, (uint32_t)__shfl_xor((int)m, off));
+            const uint32_t m = gu_wave_max(max(max(key[0], key[1]), max(key[2], key[3])));
             const uint32_t ord = m >> 16;
             const uint32_t bits = (ord & 0x8000u) ? (ord & 0x7FFFu) : (~ord & 0xFFFFu);
             sel[r] = bf16_bits_to_f32(bits);
@@ -262,8 +274,7 @@ __global__ __launch_bounds__(1024) void k_gateup_valu(GateUpArgs a) {
         acc = fmaf(p, e8m0_f32(e), acc);
     }
     // the four pieces of each row -> full row partial (lanes r, r+16, r+32, r+48)
-    acc += __shfl_xor(acc, 16);
-    acc += __shfl_xor(acc, 32);
+    acc = sum_xor32(sum_xor16(acc));
     if (TPB * ks > 1) {
         if (lane < 16) red[wave * 16 + lane] = acc;
         lds_barrier();
@@ -275,7 +286,9 @@ __global__ __launch_bounds__(1024) void k_gateup_valu(GateUpArgs a) {
     }
     if (!tile_ok) return;
     const float y = acc * ps;             // tile rows 0..7 gate, 8..15 up
-    const float u = __shfl_down(y, 8);
+    // lane r < 8 takes lane r + 8 (DPP row shift left by 8)
+    const float u = __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, y), 0x108, 0xF, 0xF, false));
     const int pair = tile * 8 + lane;
     if (lane < 8 && pair < a.inter)
         store_out(a.out, (int64_t)slot * a.inter + pair, silu(y) * u, a.out_bf16);
@@ -445,9 +458,9 @@ int device_cus() {
 }
 
 template <int UPW>
-tt_status launch_valu_upw(GateUpArgs a, int slots, hipStream_t stream) {
+tt_status launch_valu_upw(GateUpArgs a, int slots, int tpb_max, hipStream_t stream) {
     a.ks = (int32_t)ceil_div(a.units, UPW);
-    const int tpb = (a.ks * TT_GATEUP_TPB <= 8) ? TT_GATEUP_TPB : 1;
+    const int tpb = (a.ks * TT_GATEUP_TPB <= 8 && tpb_max >= TT_GATEUP_TPB) ? TT_GATEUP_TPB : 1;
     const size_t lds = (size_t)a.ks * UPW * 256 + (size_t)tpb * a.ks * 64;
     dim3 grid((unsigned)ceil_div(a.ntiles, tpb), (unsigned)slots);
     const char *what = "mxfp4 gate/up (vector path)";
@@ -459,15 +472,24 @@ tt_status launch_valu_upw(GateUpArgs a, int slots, hipStream_t stream) {
 
 // Units per wave: the tuned target, raised until a tile needs at most
 // kMaxWavesPerTile waves (K <= 16384 gives at most 128 units, so 16 units per
-// wave always suffice).
+// wave always suffice).  A grid of 4-unit waves larger than the chip holds at
+// once (8 waves per SIMD at this register count) would run a second, partial
+// round; 8-unit waves in one-tile workgroups halve the wave count instead
+// (the routed calls: batch x topk slots of every tile).
 tt_status launch_valu(GateUpArgs a, int slots, hipStream_t stream) {
     int upw = TT_GATEUP_UPW;
     while (ceil_div(a.units, upw) > kMaxWavesPerTile) upw += 4;
+    int tpb_max = TT_GATEUP_TPB;
+    if (upw == 4 && (int64_t)slots * a.ntiles * ceil_div(a.units, 4) >
+                        (int64_t)device_cus() * 4 * 8) {
+        upw = 8;
+        tpb_max = 1;
+    }
     switch (upw) {
-        case 4: return launch_valu_upw<4>(a, slots, stream);
-        case 8: return launch_valu_upw<8>(a, slots, stream);
-        case 12: return launch_valu_upw<12>(a, slots, stream);
-        case 16: return launch_valu_upw<16>(a, slots, stream);
+        case 4: return launch_valu_upw<4>(a, slots, tpb_max, stream);
+        case 8: return launch_valu_upw<8>(a, slots, tpb_max, stream);
+        case 12: return launch_valu_upw<12>(a, slots, tpb_max, stream);
+        case 16: return launch_valu_upw<16>(a, slots, tpb_max, stream);
         default: return fail(TT_E_SHAPE, "hidden = %d needs more than 8 waves per tile", a.hidden);
     }
 }
