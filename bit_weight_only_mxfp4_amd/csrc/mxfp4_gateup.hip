@@ -117,6 +117,10 @@ __device__ __forceinline__ int gu_route_topj(uint32_t key[4], int topk, int j, b
 #ifndef TT_GATEUP_TPB
 #define TT_GATEUP_TPB 2
 #endif
+// Batch 1 and the routed slots on the scaled MFMA (1) or the vector ALUs (0).
+#ifndef TT_GATEUP_MX
+#define TT_GATEUP_MX 1
+#endif
 #ifndef TT_GATEUP_MAXW
 #define TT_GATEUP_MAXW 8
 #endif
@@ -292,6 +296,266 @@ __global__ __launch_bounds__(1024) void k_gateup_valu(GateUpArgs a) {
     const int pair = tile * 8 + lane;
     if (lane < 8 && pair < a.inter)
         store_out(a.out, (int64_t)slot * a.inter + pair, silu(y) * u, a.out_bf16);
+}
+
+// Scaled-MFMA path (batch 1 and the routed slots).  The gfx950 instruction
+// v_mfma_scale_f32_16x16x128_f8f6f4 multiplies 16 x 128 FP4 (E2M1) weights
+// by 128 x 16 FP8 (E4M3) activations, each 32-element block of either side
+// multiplied by its own E8M0 scale, and accumulates in fp32.  A packed tile
+// unit is its A operand as loaded: lane l holds row l % 16, elements
+// 32 (l / 16) .. +31, and the lane's scale dword holds the E8M0 bytes of
+// that piece for four consecutive units (the byte select of the instruction
+// picks one), so the weights go to the matrix core with no conversion at all.
+// B operand (measured on the device): lane (column c, group g) holds elements
+// 16g .. 16g+15 of the unit in its first four registers and 64+16g .. +15 in
+// the next four; its scale applies to elements 32g .. 32g+31.
+// The bf16 activations are split per 32-element block into two E4M3 parts,
+//   x = 2^(E-7) hi + 2^(E-11) lo,   E = the block's largest bf16 exponent,
+// which holds exactly for every element of magnitude >= 2^(E-13) (hi carries
+// the top 4 significant bits of the 8, lo the rest) and to within 2^(E-21)
+// below that.  Token t's hi part is column t and its lo part column 8 + t;
+// column 8 + t is added onto column t after the last unit.
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+
+// Largest bf16 exponent field among the 8 elements of a 16-byte chunk.
+__device__ __forceinline__ uint32_t bf16x8_max_exp(uint4 v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = max(m, max((w[i] >> 7) & 255u, (w[i] >> 23) & 255u));
+    return m;
+}
+
+// hi and lo E4M3 parts of 4 bf16 values (2 dwords) times mult = 2^(127 - sh).
+__device__ __forceinline__ void split4(uint32_t w0, uint32_t w1, float mult, uint32_t *hi,
+                                       uint32_t *lo) {
+    const float v0 = bf16_bits_to_f32(w0 & 0xFFFFu) * mult, v1 = bf16_bits_to_f32(w0 >> 16) * mult;
+    const float v2 = bf16_bits_to_f32(w1 & 0xFFFFu) * mult, v3 = bf16_bits_to_f32(w1 >> 16) * mult;
+    int h = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+    h = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, h, true);
+    const f32x2_t b01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
+    const f32x2_t b23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
+    int l = __builtin_amdgcn_cvt_pk_fp8_f32((v0 - b01.x) * 16.0f, (v1 - b01.y) * 16.0f, 0, false);
+    l = __builtin_amdgcn_cvt_pk_fp8_f32((v2 - b23.x) * 16.0f, (v3 - b23.y) * 16.0f, l, true);
+    *hi = (uint32_t)h;
+    *lo = (uint32_t)l;
+}
+
+// One scaled MFMA, FP4 A by FP8 B; byte sel of both scale dwords (the
+// selector must be a constant: the unrolled unit index folds the switch).
+template <int SEL>
+__device__ __forceinline__ f32x4_t mfma_fp4_fp8_sel(i32x8_t A, i32x8_t B, f32x4_t C, uint32_t sa,
+                                                    uint32_t sb) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, C, 4, 0, SEL, (int)sa, SEL,
+                                                            (int)sb);
+}
+__device__ __forceinline__ f32x4_t mfma_fp4_fp8(int sel, i32x8_t A, i32x8_t B, f32x4_t C,
+                                                uint32_t sa, uint32_t sb) {
+    switch (sel) {
+        case 0: return mfma_fp4_fp8_sel<0>(A, B, C, sa, sb);
+        case 1: return mfma_fp4_fp8_sel<1>(A, B, C, sa, sb);
+        case 2: return mfma_fp4_fp8_sel<2>(A, B, C, sa, sb);
+        default: return mfma_fp4_fp8_sel<3>(A, B, C, sa, sb);
+    }
+}
+
+template <int NTOK>
+struct MxLds {
+    int kp;  // staged elements per token (a multiple of 512)
+    __device__ int q_bytes() const { return NTOK * 2 * kp; }
+    __device__ int s_bytes() const { return NTOK * 2 * (kp / 32); }
+    // E4M3 part hl (0 hi, 1 lo) of token t
+    __device__ int q_off(int t, int hl) const { return (t * 2 + hl) * kp; }
+    // E8M0 byte of part hl of token t, group g (block 4u + g) of unit u
+    __device__ int s_off(int t, int hl, int g, int u) const {
+        return q_bytes() + ((t * 2 + hl) * 4 + g) * (kp / 128) + u;
+    }
+    __device__ int zero_off() const { return q_bytes() + s_bytes(); }   // 32 zero bytes
+    __device__ int red_off() const { return zero_off() + 32; }          // [waves][NTOK][16] f32
+};
+
+template <int NTOK>
+__host__ __device__ constexpr size_t mx_lds_bytes(int ks, int upw, int tpb) {
+    return (size_t)NTOK * 2 * ks * upw * 128 + (size_t)NTOK * 2 * ks * upw * 4 + 32 +
+           (size_t)tpb * ks * NTOK * 64;
+}
+
+// Workgroup = TPB tiles x ks waves, wave (t, p) owns units [p UPW, p UPW +
+// UPW) of tile blockIdx.x * TPB + t, as on the vector path.  NTOK tokens per
+// workgroup (dense calls: tokens blockIdx.y * NTOK ..; routed calls: NTOK = 1,
+// slot blockIdx.y).  Issue order per wave: its share of the activations,
+// then each scale dword followed by its four units, then the postscales;
+// the activations are split into their E4M3 parts into LDS, and after an
+// LDS-only barrier each unit goes to the matrix core as its load lands.
+template <int UPW, int TPB, int NTOK>
+__global__ __launch_bounds__(1024) void k_gateup_mx(GateUpArgs a) {
+    static_assert(UPW % 4 == 0 && UPW <= 16, "units per wave");
+    static_assert(NTOK == 1 || NTOK == 2 || NTOK == 4 || NTOK == 8, "tokens per workgroup");
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int ks = a.ks;
+    const MxLds<NTOK> L{ks * UPW * 128};
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int nthreads = blockDim.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tsub = wave / ks, part = wave - tsub * ks;
+    const int tile = blockIdx.x * TPB + tsub, slot = blockIdx.y;
+    const bool routed = a.ids || a.logits;
+    const int tok0 = routed ? slot / a.topk : slot * NTOK;   // first token of the workgroup
+    const int ntok = routed ? 1 : min(NTOK, a.batch - tok0);
+
+    // 1. activations: 16-byte chunks, NTOK * kp / 8 of them (zero past K
+    //    and past the batch); chunk i of a token is elements 8i .. 8i+7
+    constexpr int XC = NTOK * UPW / 4;   // >= chunks per thread (nthreads >= 64 ks)
+    const int tchunks = L.kp / 8, xvalid = a.hidden / 8;
+    uint4 xv[XC];
+#pragma unroll
+    for (int j = 0; j < XC; ++j) {
+        const int idx = tid + j * nthreads, t = idx / tchunks, ci = idx - t * tchunks;
+        xv[j] = (t < ntok && ci < xvalid)
+                    ? reinterpret_cast<const uint4 *>(a.x + (int64_t)(tok0 + t) * a.hidden)[ci]
+                    : make_uint4(0, 0, 0, 0);
+    }
+
+    const uint8_t *base = a.w;
+    if (a.logits) {
+        const uint16_t *lb = a.logits + (int64_t)tok0 * a.n_experts;
+        uint32_t key[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ei = lane + 64 * i;
+            key[i] = 0u;
+            if (64 * i < a.n_experts) {  // uniform
+                const uint32_t raw = lb[min(ei, a.n_experts - 1)];
+                key[i] = ei < a.n_experts ? gu_route_key(raw, ei) : 0u;
+            }
+        }
+        float wj = 0.0f;
+        const int j = slot - tok0 * a.topk;
+        const bool writer = blockIdx.x == 0;
+        const int e = gu_route_topj(key, a.topk, j, writer, &wj);
+        if (writer && tid == 0) {
+            a.ids_out[slot] = e;
+            a.w_out[slot] = wj;
+        }
+        base += (int64_t)e * a.expert_stride;
+    } else if (a.ids) {
+        const int e = a.ids[slot];
+        if (e < 0 || e >= a.n_experts) {
+            for (int i = tid; i < TPB * 8; i += nthreads) {
+                const int pair = blockIdx.x * TPB * 8 + i;
+                if (pair < a.inter)
+                    store_out(a.out, (int64_t)slot * a.inter + pair, __builtin_nanf(""),
+                              a.out_bf16);
+            }
+            return;
+        }
+        base += (int64_t)e * a.expert_stride;
+    }
+
+    // 2. weights
+    const bool tile_ok = tile < a.ntiles;
+    const uint8_t *tb = base + (int64_t)(tile_ok ? tile : 0) * a.tile_stride;
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(tb, a.tile_stride);
+    const int u0 = part * UPW;
+    const int n = tile_ok ? max(0, min(UPW, a.units - u0)) : 0;
+    uint4 c[UPW];
+    uint32_t sd[UPW / 4];
+    const int voff = u0 * kUnitBytes + lane * 16;
+    const int soff = a.scale_off + (u0 >> 2) * kGroupBytes + lane * 4;
+#pragma unroll
+    for (int g = 0; g < UPW / 4; ++g) {
+        sd[g] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * g < n ? soff + g * kGroupBytes : kOob,
+                                                     0, 0);
+#pragma unroll
+        for (int i = 4 * g; i < 4 * g + 4; ++i)
+            c[i] = load16(rs, i < n ? voff + i * kUnitBytes : kOob);
+    }
+    // postscales of gate row r and up row r + 8 for the finishing lanes
+    // (lane 8t + r, r < 8), fetched with the weights
+    const int fr = lane & 7;
+    const bool fin = part == 0 && tile_ok;
+    const float psg = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rs, fin ? a.ps_off + fr * 4 : kOob, 0, 0));
+    const float psu = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rs, fin ? a.ps_off + (fr + 8) * 4 : kOob, 0, 0));
+    // keep every load above the activation split
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 3. activations -> E4M3 parts and their scales in LDS.  The four chunks
+    //    of a 32-element block sit in four consecutive lanes; their largest
+    //    exponent is shared through two DPP quad swaps.
+#pragma unroll
+    for (int j = 0; j < XC; ++j) {
+        const int idx = tid + j * nthreads, t = idx / tchunks, ci = idx - t * tchunks;
+        uint32_t e = bf16x8_max_exp(xv[j]);
+        e = max(e, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)e, 0xB1, 0xF, 0xF, false));
+        e = max(e, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)e, 0x4E, 0xF, 0xF, false));
+        if (t < NTOK) {
+            // scale byte of the hi part: 2^(E-7) with E = e - 127, kept in
+            // [5, 254] (the lo part's byte is 4 less)
+            const uint32_t sh = min(max(e, 12u) - 7u, 254u);
+            const float mult = __builtin_bit_cast(float, (254u - sh) << 23);
+            uint32_t h0, h1, l0, l1;
+            split4(xv[j].x, xv[j].y, mult, &h0, &l0);
+            split4(xv[j].z, xv[j].w, mult, &h1, &l1);
+            *reinterpret_cast<uint2 *>(smem + L.q_off(t, 0) + ci * 8) = make_uint2(h0, h1);
+            *reinterpret_cast<uint2 *>(smem + L.q_off(t, 1) + ci * 8) = make_uint2(l0, l1);
+            if ((ci & 3) == 0) {
+                const int blk = ci >> 2;
+                smem[L.s_off(t, 0, blk & 3, blk >> 2)] = (uint8_t)sh;
+                smem[L.s_off(t, 1, blk & 3, blk >> 2)] = (uint8_t)(sh - 4u);
+            }
+        }
+    }
+    if (tid < 8) reinterpret_cast<uint32_t *>(smem + L.zero_off())[tid] = 0u;
+    lds_barrier();
+
+    // 4. the units in load order, one scaled MFMA each
+    const int col = lane & 15, grp = lane >> 4;
+    const int ct = col & 7, hl = col >> 3;
+    const bool bact = ct < ntok;
+    const int qbase = bact ? L.q_off(ct, hl) + u0 * 128 + 16 * grp : L.zero_off();
+    const int qstep = bact ? 128 : 0;
+    const int sbase = L.s_off(bact ? ct : 0, hl, grp, u0);
+    f32x4_t C = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    uint32_t sb = 0x7F7F7F7Fu;  // columns without a token: scale 1, zero data
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+        if ((i & 3) == 0 && bact) sb = *reinterpret_cast<const uint32_t *>(smem + sbase + i);
+        const uint4 b0 = *reinterpret_cast<const uint4 *>(smem + qbase + i * qstep);
+        const uint4 b1 = *reinterpret_cast<const uint4 *>(smem + qbase + i * qstep + (bact ? 64 : 16));
+        const i32x8_t B = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                           (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+        const i32x8_t A = {(int)c[i].x, (int)c[i].y, (int)c[i].z, (int)c[i].w, 0, 0, 0, 0};
+        C = mfma_fp4_fp8(i & 3, A, B, C, sd[i >> 2], sb);
+    }
+
+    // 5. lo column 8 + t onto column t (DPP row shift left by 8), the
+    //    partial rows to LDS, one barrier, then the fixed-order sum over the
+    //    K parts by the tile's first wave: lane 8t + r finishes pair r of
+    //    token t (gate row r, up row r + 8)
+    const u32x4_t cw = __builtin_bit_cast(u32x4_t, C);
+    f32x4_t y;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        y[r] = C[r] + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, (int)cw[r], 0x108,
+                                                                            0xF, 0xF, false));
+    float *red = reinterpret_cast<float *>(smem + L.red_off());
+    if (col < ntok)  // lane (t, g): rows 4g .. 4g+3 of token t
+        *reinterpret_cast<f32x4_t *>(red + (wave * NTOK + col) * 16 + 4 * grp) = y;
+    lds_barrier();
+    const int ft = lane >> 3;
+    if (part != 0 || !tile_ok || ft >= ntok) return;
+    float g = 0.0f, u = 0.0f;
+    for (int p = 0; p < ks; ++p) {
+        const float *rp = red + ((tsub * ks + p) * NTOK + ft) * 16;
+        g += rp[fr];
+        u += rp[fr + 8];
+    }
+    const int pair = tile * 8 + fr;
+    const int orow = routed ? slot : tok0 + ft;
+    if (pair < a.inter)
+        store_out(a.out, (int64_t)orow * a.inter + pair, silu(g * psg) * (u * psu), a.out_bf16);
 }
 
 // MFMA path (batch 2..32).  NCOL column blocks of 16 tokens.  A workgroup of
@@ -470,21 +734,44 @@ tt_status launch_valu_upw(GateUpArgs a, int slots, int tpb_max, hipStream_t stre
                   stream, a);
 }
 
+template <int UPW, int NTOK>
+tt_status launch_mx_upw(GateUpArgs a, int slots, int tpb_max, hipStream_t stream) {
+    a.ks = (int32_t)ceil_div(a.units, UPW);
+    const int tpb = (a.ks * TT_GATEUP_TPB <= 8 && tpb_max >= TT_GATEUP_TPB) ? TT_GATEUP_TPB : 1;
+    const size_t lds = mx_lds_bytes<NTOK>(a.ks, UPW, tpb);
+    dim3 grid((unsigned)ceil_div(a.ntiles, tpb), (unsigned)slots);
+    const char *what = "mxfp4 gate/up (scaled MFMA)";
+    if (tpb == 1)
+        return launch(what, k_gateup_mx<UPW, 1, NTOK>, grid, dim3(64 * a.ks), lds, stream, a);
+    return launch(what, k_gateup_mx<UPW, TT_GATEUP_TPB, NTOK>, grid, dim3(64 * tpb * a.ks), lds,
+                  stream, a);
+}
+
 // Units per wave: the tuned target, raised until a tile needs at most
-// kMaxWavesPerTile waves (K <= 16384 gives at most 128 units, so 16 units per
-// wave always suffice).  A grid of 4-unit waves larger than the chip holds at
-// once (8 waves per SIMD at this register count) would run a second, partial
-// round; 8-unit waves in one-tile workgroups halve the wave count instead
-// (the routed calls: batch x topk slots of every tile).
+// kMaxWavesPerTile waves (16 on the scaled-MFMA path, K <= 16384 gives at
+// most 128 units, so 8 units per wave always suffice; 8 on the vector path).
+// A grid of 4-unit waves that overflows what the chip holds at once (7-8
+// waves per SIMD at these register counts) but fits it with 8-unit waves in
+// one-tile workgroups switches to those: the routed calls, batch x topk
+// slots of every tile, would otherwise run a second, partial round.
 tt_status launch_valu(GateUpArgs a, int slots, hipStream_t stream) {
+    const int maxw = TT_GATEUP_MX ? 16 : kMaxWavesPerTile;
     int upw = TT_GATEUP_UPW;
-    while (ceil_div(a.units, upw) > kMaxWavesPerTile) upw += 4;
+    while (ceil_div(a.units, upw) > maxw) upw += 4;
     int tpb_max = TT_GATEUP_TPB;
-    if (upw == 4 && (int64_t)slots * a.ntiles * ceil_div(a.units, 4) >
-                        (int64_t)device_cus() * 4 * 8) {
+    const int64_t resident = (int64_t)device_cus() * 4 * 7;
+    if (upw == 4 && (int64_t)slots * a.ntiles * ceil_div(a.units, 4) > resident &&
+        (int64_t)slots * a.ntiles * ceil_div(a.units, 8) <= resident) {
         upw = 8;
         tpb_max = 1;
     }
+#if TT_GATEUP_MX
+    switch (upw) {
+        case 4: return launch_mx_upw<4, 1>(a, slots, tpb_max, stream);
+        case 8: return launch_mx_upw<8, 1>(a, slots, tpb_max, stream);
+        default: return fail(TT_E_SHAPE, "hidden = %d needs more than 16 waves per tile", a.hidden);
+    }
+#else
     switch (upw) {
         case 4: return launch_valu_upw<4>(a, slots, tpb_max, stream);
         case 8: return launch_valu_upw<8>(a, slots, tpb_max, stream);
@@ -492,6 +779,7 @@ tt_status launch_valu(GateUpArgs a, int slots, hipStream_t stream) {
         case 16: return launch_valu_upw<16>(a, slots, tpb_max, stream);
         default: return fail(TT_E_SHAPE, "hidden = %d needs more than 8 waves per tile", a.hidden);
     }
+#endif
 }
 
 constexpr size_t kMaxLds = 160 * 1024;
