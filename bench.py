@@ -178,7 +178,7 @@ def run(args):
         per_call = gateup_bytes(w.inter, w.hidden, batch)
         us_call = secs / calls * 1e6
         gbs = per_call * calls / secs / 1e9
-        kernel = "k_gateup_valu" if batch == 1 else "k_gateup_mfma"
+        kernel = "k_gateup_mx" if batch <= 2 else "k_gateup_mfma"
         result = dict(metric="effective HBM GB/s of the MXFP4 gate/up SwiGLU GEMV "
                              "(us/call alongside)",
                       value=round(gbs, 2), unit="GB/s", us_per_call=round(us_call, 3),
@@ -287,7 +287,7 @@ def run(args):
                                   routing="a distinct seeded routing per layer, fused into "
                                           "the expert gate/up call",
                                   launch="one HIP graph per step"),
-                      roofline=dict(bound="hbm", kernel="k_gateup_valu(routed)+k_down_combine",
+                      roofline=dict(bound="hbm", kernel="k_gateup_mx(routed)+k_down_combine",
                                     achieved=round(gbs, 2), peak=PEAK_HBM_GBS, unit="GB/s",
                                     frac=round(gbs / PEAK_HBM_GBS, 4),
                                     traffic=profiled_traffic(
@@ -474,7 +474,9 @@ def run(args):
              "attention": "bf16 x bf16 -> fp32 accumulate",
              "fp8-down": "fp8-e4m3 x fp32 -> fp32 accumulate",
              "quantize": "fp32 -> fp4-e2m1 + e8m0 (host)"}.get(
-                 args.workload, "fp4-e2m1 x bf16 -> fp32 accumulate")
+                 args.workload, "fp4-e2m1 x bf16 (two e4m3 parts) -> fp32 accumulate")
+    if args.workload == "batched" and args.batch > 2:
+        dtype = "fp4-e2m1 x bf16 -> fp32 accumulate"
     result.update(n_gpus=1, steps=K, warmup=W, higher_is_better=True, scaling="strong",
                   vs_baseline=None, dtype=dtype,
                   data="synthetic (seeded codes, scales, postscales, activations)")

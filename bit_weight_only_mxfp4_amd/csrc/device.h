@@ -29,33 +29,10 @@ __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) {
     return __builtin_bit_cast(bf16x2_t, v);
 }
 
-// The 8 FP4 codes of one dword (code 2j in bits 8j..8j+3, code 2j+1 in bits
-// 8j+4..8j+7) against 8 bf16 activations held as 4 packed pairs.  Each
-// conversion turns one byte (two codes) into two exact bf16 values; the dot2
-// multiplies them with the matching activation pair and accumulates in fp32.
-__device__ __forceinline__ float fp4x8_dot_bf16(uint32_t c, uint4 x, float acc) {
-    acc = __builtin_amdgcn_fdot2_f32_bf16(
-        __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 0), as_bf16x2(x.x), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(
-        __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 1), as_bf16x2(x.y), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(
-        __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 2), as_bf16x2(x.z), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(
-        __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, 3), as_bf16x2(x.w), acc, false);
-    return acc;
-}
-
-// One 32-element MX block (16 code bytes) against 32 bf16 activations
-// (4 x 16 bytes), unscaled.  Two accumulators shorten the dependency chain.
-__device__ __forceinline__ float fp4x32_dot_bf16(uint4 c, const uint4 *x) {
-    float p0 = fp4x8_dot_bf16(c.x, x[0], 0.0f);
-    float p1 = fp4x8_dot_bf16(c.y, x[1], 0.0f);
-    p0 = fp4x8_dot_bf16(c.z, x[2], p0);
-    p1 = fp4x8_dot_bf16(c.w, x[3], p1);
-    return p0 + p1;
-}
-
-// The same block against fp32 activations (8 x 16 bytes).
+// One 32-element MX block (16 code bytes: code 2j in bits 8j..8j+3, code
+// 2j+1 in bits 8j+4..8j+7 of its byte) against fp32 activations (8 x 16
+// bytes), unscaled: the hardware FP4 conversion gives exact fp32 pairs, one
+// FMA per element, two accumulators to shorten the dependency chain.
 __device__ __forceinline__ float fp4x8_dot_f32(uint32_t c, float4 xa, float4 xb, float acc) {
     f32x2_t v;
     v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
@@ -137,14 +114,76 @@ __device__ __forceinline__ void store_out(void *out, int64_t i, float v, int bf1
         static_cast<float *>(out)[i] = v;
 }
 
-// Stage n bf16 activations into LDS, zero-filling up to n_pad (both
-// multiples of 8); 16-byte chunks, all threads of the block cooperate.
-__device__ __forceinline__ void stage_bf16(uint16_t *dst, const uint16_t *src, int n,
-                                           int n_pad, int tid, int nthreads) {
-    const uint4 *s = reinterpret_cast<const uint4 *>(src);
-    uint4 *d = reinterpret_cast<uint4 *>(dst);
-    for (int i = tid; i < n_pad / 8; i += nthreads)
-        d[i] = (i < n / 8) ? s[i] : make_uint4(0, 0, 0, 0);
+// ---- scaled FP4 x FP8 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4) -----------
+// A (16 x 128, FP4 E2M1, 4 registers): lane l holds row l % 16, elements
+// 32 (l / 16) .. +31 -- exactly one packed tile unit as loaded; A scale: the
+// lane's E8M0 byte for that 32-element piece.  B (128 x 16, FP8 E4M3, 8
+// registers): lane (column c = l % 16, group g = l / 16) holds elements
+// 16g .. 16g+15 in its first four registers and 64+16g .. +15 in the next
+// four; B scale of lane (c, g): the E8M0 byte of elements 32g .. 32g+31.
+// Output: lane (c, g) holds rows 4g .. 4g+3 of column c.  (Layouts measured
+// on the device.)  Activations enter as two E4M3 parts per 32-element block,
+//   x = 2^(E-7) hi + 2^(E-11) lo,   E = the block's largest bf16 exponent,
+// exact for every element of magnitude >= 2^(E-13) (hi carries the top 4
+// of the 8 significant bits, lo the rest) and to within 2^(E-21) below.
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+
+// Largest bf16 exponent field among the 8 elements of a 16-byte chunk.
+__device__ __forceinline__ uint32_t bf16x8_max_exp(uint4 v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = max(m, max((w[i] >> 7) & 255u, (w[i] >> 23) & 255u));
+    return m;
+}
+
+// hi and lo E4M3 parts of 4 bf16 values (2 dwords) times mult = 2^(127 - sh).
+__device__ __forceinline__ void split4(uint32_t w0, uint32_t w1, float mult, uint32_t *hi,
+                                       uint32_t *lo) {
+    const float v0 = bf16_bits_to_f32(w0 & 0xFFFFu) * mult, v1 = bf16_bits_to_f32(w0 >> 16) * mult;
+    const float v2 = bf16_bits_to_f32(w1 & 0xFFFFu) * mult, v3 = bf16_bits_to_f32(w1 >> 16) * mult;
+    int h = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+    h = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, h, true);
+    const f32x2_t b01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
+    const f32x2_t b23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
+    int l = __builtin_amdgcn_cvt_pk_fp8_f32((v0 - b01.x) * 16.0f, (v1 - b01.y) * 16.0f, 0, false);
+    l = __builtin_amdgcn_cvt_pk_fp8_f32((v2 - b23.x) * 16.0f, (v3 - b23.y) * 16.0f, l, true);
+    *hi = (uint32_t)h;
+    *lo = (uint32_t)l;
+}
+
+// The two E4M3 parts of one 16-byte chunk (8 bf16) of a 32-element block
+// whose four chunks sit in four consecutive lanes (their largest exponent is
+// shared through two DPP quad swaps, so all 64 lanes must take part).
+// Returns the hi part's E8M0 byte, 2^(E-7) kept in [5, 254]; the lo part's
+// byte is 4 less.  Zero chunks give zero parts.
+__device__ __forceinline__ uint32_t split_chunk(uint4 v, uint2 *hi, uint2 *lo) {
+    uint32_t e = bf16x8_max_exp(v);
+    e = max(e, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)e, 0xB1, 0xF, 0xF, false));
+    e = max(e, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)e, 0x4E, 0xF, 0xF, false));
+    const uint32_t sh = min(max(e, 12u) - 7u, 254u);
+    const float mult = __builtin_bit_cast(float, (254u - sh) << 23);  // 2^(127 - sh)
+    split4(v.x, v.y, mult, &hi->x, &lo->x);
+    split4(v.z, v.w, mult, &hi->y, &lo->y);
+    return sh;
+}
+
+// One scaled MFMA, FP4 A by FP8 B; byte sel of both scale dwords (the
+// selector must be a constant: the unrolled unit index folds the switch).
+template <int SEL>
+__device__ __forceinline__ f32x4_t mfma_fp4_fp8_sel(i32x8_t A, i32x8_t B, f32x4_t C, uint32_t sa,
+                                                    uint32_t sb) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, C, 4, 0, SEL, (int)sa, SEL,
+                                                            (int)sb);
+}
+__device__ __forceinline__ f32x4_t mfma_fp4_fp8(int sel, i32x8_t A, i32x8_t B, f32x4_t C,
+                                                uint32_t sa, uint32_t sb) {
+    switch (sel) {
+        case 0: return mfma_fp4_fp8_sel<0>(A, B, C, sa, sb);
+        case 1: return mfma_fp4_fp8_sel<1>(A, B, C, sa, sb);
+        case 2: return mfma_fp4_fp8_sel<2>(A, B, C, sa, sb);
+        default: return mfma_fp4_fp8_sel<3>(A, B, C, sa, sb);
+    }
 }
 
 // Launch a kernel whose only parameter is an argument struct and report the

@@ -11,9 +11,11 @@
 //
 // Down + combine: one workgroup per (16-row tile of the output, token) with
 // topk * S waves -- wave (j, part) streams expert ids[b][j]'s tile over its
-// share of the K units against h[b][j] staged in LDS.  The per-row partials
-// are combined in a fixed order (parts, then slots j = 0..topk-1), so there
-// are no atomics and the result is bit-reproducible.
+// share of the K units against h[b][j] staged in LDS: bf16 h on the scaled
+// FP4 x FP8 MFMA (the expert's packed units as A operands, h split into two
+// E4M3 parts as B), fp32 h on the vector ALUs.  The per-row partials are
+// combined in a fixed order (parts, then slots j = 0..topk-1), so there are
+// no atomics and the result is bit-reproducible.
 #include <algorithm>
 
 #include "device.h"
@@ -112,16 +114,17 @@ __device__ __forceinline__ void down_lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// One workgroup per (16-row output tile, token).  Slots are processed in
-// rounds of spr; within a round wave (slot j, part p) owns units
+// fp32 h (vector ALUs; bf16 h takes the scaled-MFMA kernel below).  One
+// workgroup per (16-row output tile, token).  Slots are processed in rounds
+// of spr; within a round wave (slot j, part p) owns units
 // [p * UPW, p * UPW + UPW) of expert ids[b][j]'s tile.  Issue order per wave:
 // its share of the round's activations, then each scale dword followed by its
 // four code units, then the postscales.  A slot with a bad expert id gets a
 // zero-length buffer descriptor, so its loads read nothing and return zeros.
-template <int UPW, bool HF32>
+template <int UPW>
 __global__ __launch_bounds__(1024) void k_down_combine(DownArgs a) {
     static_assert(UPW % 4 == 0 && UPW <= 16, "units per wave");
-    constexpr int ESZ = HF32 ? 4 : 2;
+    constexpr int ESZ = 4;                       // fp32 h
     constexpr int XC = UPW * ESZ / 8;            // 16-byte chunks per thread per round
     extern __shared__ __align__(16) uint8_t smem[];
     const int S = a.S, topk = a.topk, spr = a.spr;
@@ -194,20 +197,12 @@ __global__ __launch_bounds__(1024) void k_down_combine(DownArgs a) {
 
         // 4. consume the units in load order
         float acc = 0.0f;
-        if (HF32) {
-            const float4 *xb = reinterpret_cast<const float4 *>(smem) +
-                               ((size_t)js * kp + (4 * u0 + q) * 32) / 4;
+        const float4 *xb = reinterpret_cast<const float4 *>(smem) +
+                           ((size_t)js * kp + (4 * u0 + q) * 32) / 4;
 #pragma unroll
-            for (int i = 0; i < UPW; ++i)
-                acc = fmaf(fp4x32_dot_f32(c[i], xb + i * 32),
-                           e8m0_f32((sd[i >> 2] >> (8 * (i & 3))) & 255u), acc);
-        } else {
-            const uint4 *xb = xs4 + ((size_t)js * kp + (4 * u0 + q) * 32) / 8;
-#pragma unroll
-            for (int i = 0; i < UPW; ++i)
-                acc = fmaf(fp4x32_dot_bf16(c[i], xb + i * 16),
-                           e8m0_f32((sd[i >> 2] >> (8 * (i & 3))) & 255u), acc);
-        }
+        for (int i = 0; i < UPW; ++i)
+            acc = fmaf(fp4x32_dot_f32(c[i], xb + i * 32),
+                       e8m0_f32((sd[i >> 2] >> (8 * (i & 3))) & 255u), acc);
         acc = sum_xor32(sum_xor16(acc));
         if (slot_ok) {
             if (lane < 16) red[(j * S + part) * 16 + lane] = acc;
@@ -229,26 +224,178 @@ __global__ __launch_bounds__(1024) void k_down_combine(DownArgs a) {
     if (row < a.hidden) store_out(a.y, (int64_t)b * a.hidden + row, y, a.y_bf16);
 }
 
+// Scaled-MFMA form of the same kernel for bf16 h: each unit goes to
+// v_mfma_scale_f32_16x16x128_f8f6f4 with the expert's packed unit and its
+// E8M0 bytes as the A operand and the slot's h, split per 32-element block
+// into two E4M3 parts (device.h), as B column 0 (hi) and column 8 (lo).
+// LDS: the parts [spr][2][kp] bytes, their scale bytes [spr][2][4][kp/128],
+// 32 zero bytes (B of the unused columns), then the partial rows and the
+// postscales / weights of the combine.
+template <int UPW>
+__global__ __launch_bounds__(1024) void k_down_mx(DownArgs a) {
+    static_assert(UPW % 4 == 0 && UPW <= 16, "units per wave");
+    constexpr int XC = UPW / 4;                  // 16-byte chunks per thread per round
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int S = a.S, topk = a.topk, spr = a.spr;
+    const int kp = S * UPW * 128;                // staged K per slot, zero past inter
+    const int kpc = kp / 8, kpu = kp / 128;
+    const int qsz = spr * 2 * kp, zoff = qsz + spr * kp / 16;
+    float *red = reinterpret_cast<float *>(smem + zoff + 32);  // [topk][S][16]
+    float *pss = red + topk * S * 16;                          // [topk][17]
+    const int tid = threadIdx.x, lane = tid & 63, nthreads = blockDim.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tile = blockIdx.x, b = blockIdx.y;
+    const int js = wave / S, part = wave - js * S;
+    const int valid_chunks = a.inter / 8;
+    const uint4 *hsrc = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.h) +
+                                                        (size_t)b * topk * a.inter);
+    const int col = lane & 15, grp = lane >> 4, hl = col >> 3;
+    const bool bact = (col & 7) == 0;            // columns 0 (hi) and 8 (lo)
+
+    for (int jb = 0; jb < topk; jb += spr) {
+        const int j = jb + js;
+        const bool slot_ok = j < topk;
+        const int e = slot_ok ? a.ids[b * topk + j] : -1;
+        const bool valid = e >= 0 && e < a.n_experts;
+
+        // 1. activations of slots jb .. jb + spr - 1 (XC * nthreads = spr * kpc)
+        uint4 hv[XC];
+#pragma unroll
+        for (int c = 0; c < XC; ++c) {
+            const int idx = tid + c * nthreads;
+            const int jj = jb + idx / kpc, off = idx % kpc;
+            hv[c] = (jj < topk && off < valid_chunks) ? hsrc[jj * valid_chunks + off]
+                                                     : make_uint4(0, 0, 0, 0);
+        }
+
+        // 2. weights
+        const uint8_t *tb = valid ? a.bank + (int64_t)e * a.expert_stride +
+                                        (int64_t)tile * a.tile_stride
+                                  : a.bank;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t *>(tb), 0, valid ? (int)a.tile_stride : 0, 0x00020000);
+        const int u0 = part * UPW;
+        const int n = max(0, min(UPW, a.units - u0));
+        uint4 c[UPW];
+        uint32_t sd[UPW / 4];
+        const int voff = u0 * kUnitBytes + lane * 16;
+        const int soff = a.scale_off + (u0 >> 2) * kGroupBytes + lane * 4;
+#pragma unroll
+        for (int g = 0; g < UPW / 4; ++g) {
+            sd[g] = __builtin_amdgcn_raw_buffer_load_b32(
+                rs, 4 * g < n ? soff + g * kGroupBytes : kDownOob, 0, 0);
+#pragma unroll
+            for (int i = 4 * g; i < 4 * g + 4; ++i) {
+                const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
+                    rs, i < n ? voff + i * kUnitBytes : kDownOob, 0, 0);
+                c[i] = make_uint4(v.x, v.y, v.z, v.w);
+            }
+        }
+        const float ps = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(
+                       rs, (part == 0 && lane < 16) ? a.ps_off + lane * 4 : kDownOob, 0, 0));
+        const float wj = slot_ok ? a.wt[b * topk + j] : 0.0f;
+        __builtin_amdgcn_sched_barrier(0);
+
+        // 3. activations -> E4M3 parts in LDS (after the previous round
+        //    finished reading)
+        if (jb > 0) down_lds_barrier();
+#pragma unroll
+        for (int cc = 0; cc < XC; ++cc) {
+            const int idx = tid + cc * nthreads;
+            const int jl = idx / kpc, ci = idx % kpc;
+            uint2 hi, lo;
+            const uint32_t sh = split_chunk(hv[cc], &hi, &lo);
+            *reinterpret_cast<uint2 *>(smem + (jl * 2) * kp + ci * 8) = hi;
+            *reinterpret_cast<uint2 *>(smem + (jl * 2 + 1) * kp + ci * 8) = lo;
+            if ((ci & 3) == 0) {
+                const int blk = ci >> 2;
+                smem[qsz + ((jl * 2) * 4 + (blk & 3)) * kpu + (blk >> 2)] = (uint8_t)sh;
+                smem[qsz + ((jl * 2 + 1) * 4 + (blk & 3)) * kpu + (blk >> 2)] = (uint8_t)(sh - 4u);
+            }
+        }
+        if (tid < 8) reinterpret_cast<uint32_t *>(smem + zoff)[tid] = 0u;
+        down_lds_barrier();
+
+        // 4. the units in load order, one scaled MFMA each
+        const int qbase = bact ? (js * 2 + hl) * kp + u0 * 128 + 16 * grp : zoff;
+        const int qstep = bact ? 128 : 0, qhalf = bact ? 64 : 16;
+        const int sbase = qsz + ((js * 2 + hl) * 4 + grp) * kpu + u0;
+        f32x4_t C = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        uint32_t sb = 0x7F7F7F7Fu;
+#pragma unroll
+        for (int i = 0; i < UPW; ++i) {
+            if ((i & 3) == 0 && bact) sb = *reinterpret_cast<const uint32_t *>(smem + sbase + i);
+            const uint4 b0 = *reinterpret_cast<const uint4 *>(smem + qbase + i * qstep);
+            const uint4 b1 = *reinterpret_cast<const uint4 *>(smem + qbase + i * qstep + qhalf);
+            const i32x8_t B = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                               (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+            const i32x8_t A = {(int)c[i].x, (int)c[i].y, (int)c[i].z, (int)c[i].w, 0, 0, 0, 0};
+            C = mfma_fp4_fp8(i & 3, A, B, C, sd[i >> 2], sb);
+        }
+        // 5. lo column 8 onto column 0 (DPP row shift left by 8); lane
+        //    (0, g) holds rows 4g .. 4g+3
+        const u32x4_t cw = __builtin_bit_cast(u32x4_t, C);
+        f32x4_t y;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            y[r] = C[r] + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                        0, (int)cw[r], 0x108, 0xF, 0xF, false));
+        if (slot_ok) {
+            if (col == 0) *reinterpret_cast<f32x4_t *>(red + (j * S + part) * 16 + 4 * grp) = y;
+            if (part == 0 && lane < 16) pss[j * 17 + lane] = ps;
+            if (part == 0 && lane == 16) pss[j * 17 + 16] = valid ? wj : __builtin_nanf("");
+        }
+    }
+    down_lds_barrier();
+    if (wave != 0 || lane >= 16) return;
+    float y = 0.0f;
+    for (int jj = 0; jj < topk; ++jj) {
+        float dot = red[(jj * S) * 16 + lane];
+        for (int pp = 1; pp < S; ++pp) dot += red[(jj * S + pp) * 16 + lane];
+        y += pss[jj * 17 + 16] * (pss[jj * 17 + lane] * dot);
+    }
+    const int row = tile * 16 + lane;
+    if (row < a.hidden) store_out(a.y, (int64_t)b * a.hidden + row, y, a.y_bf16);
+}
+
 }  // namespace tt
 
 namespace tt {
 namespace {
 
-template <int UPW, bool HF32>
-tt_status launch_down(const DownArgs &a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+template <int UPW>
+tt_status launch_down_mx(const DownArgs &a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
     if (lds > 64 * 1024) {
         static bool raised[64] = {false};
         int dev = 0;
         (void)hipGetDevice(&dev);
         if (dev >= 0 && dev < 64 && !raised[dev]) {
-            if (hipFuncSetAttribute(reinterpret_cast<const void *>(k_down_combine<UPW, HF32>),
+            if (hipFuncSetAttribute(reinterpret_cast<const void *>(k_down_mx<UPW>),
                                     hipFuncAttributeMaxDynamicSharedMemorySize,
                                     160 * 1024) != hipSuccess)
                 return fail(TT_E_HIP, "cannot raise the LDS limit of the down kernel");
             raised[dev] = true;
         }
     }
-    return launch("moe down + combine", k_down_combine<UPW, HF32>, grid, block, lds, s, a);
+    return launch("moe down + combine (scaled MFMA)", k_down_mx<UPW>, grid, block, lds, s, a);
+}
+
+template <int UPW>
+tt_status launch_down(const DownArgs &a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+    if (lds > 64 * 1024) {
+        static bool raised[64] = {false};
+        int dev = 0;
+        (void)hipGetDevice(&dev);
+        if (dev >= 0 && dev < 64 && !raised[dev]) {
+            if (hipFuncSetAttribute(reinterpret_cast<const void *>(k_down_combine<UPW>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    160 * 1024) != hipSuccess)
+                return fail(TT_E_HIP, "cannot raise the LDS limit of the down kernel");
+            raised[dev] = true;
+        }
+    }
+    return launch("moe down + combine", k_down_combine<UPW>, grid, block, lds, s, a);
 }
 
 }  // namespace
@@ -316,32 +463,38 @@ extern "C" tt_status tt_moe_mxfp4_down_combine(const void *down_bank, int64_t n_
     a.topk = (int32_t)topk;
     a.y = y;
     a.y_bf16 = y_dtype == TT_BF16;
-    // waves per slot S = ceil(units / UPW), slots per round so that a
-    // workgroup holds at most 16 waves
+    // waves per slot S = ceil(units / UPW) <= 16 (inter <= TT_MAX_K gives at
+    // most 128 units), slots per round so that a workgroup holds at most 16
+    // waves
     int upw = TT_DOWN_UPW;
     while (ceil_div(g.units, upw) > 16) upw += 4;
+    if (upw > 8) return fail(TT_E_SHAPE, "inter = %lld is too long", (long long)inter);
     a.S = (int32_t)ceil_div(g.units, upw);
     a.spr = (int32_t)std::max<int64_t>(1, std::min<int64_t>(topk, 16 / a.S));
-    const size_t esz = h_dtype == TT_F32 ? 4 : 2;
-    const size_t lds = (size_t)a.spr * a.S * upw * 128 * esz + (size_t)topk * a.S * 64 +
+    dim3 grid((unsigned)ceil_div(hidden, kTileRows), (unsigned)batch);
+    dim3 block((unsigned)(64 * a.S * a.spr));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (h_dtype == TT_BF16) {
+        // scaled MFMA: E4M3 parts + scale bytes + zero bytes + partials
+        const size_t kp = (size_t)a.S * upw * 128;
+        const size_t lds = (size_t)a.spr * 2 * kp + (size_t)a.spr * kp / 16 + 32 +
+                           (size_t)topk * a.S * 64 + (size_t)topk * 17 * 4;
+        if (lds > 160 * 1024)
+            return fail(TT_E_SHAPE, "inter = %lld: the staged activations do not fit in LDS",
+                        (long long)inter);
+        const tt_status st = upw == 4 ? launch_down_mx<4>(a, grid, block, lds, s)
+                                      : launch_down_mx<8>(a, grid, block, lds, s);
+        if (st == TT_OK) clear_error();
+        return st;
+    }
+    // fp32 h on the vector ALUs
+    const size_t lds = (size_t)a.spr * a.S * upw * 128 * 4 + (size_t)topk * a.S * 64 +
                        (size_t)topk * 17 * 4;
     if (lds > 160 * 1024)
         return fail(TT_E_SHAPE, "inter = %lld: the staged activations do not fit in LDS",
                     (long long)inter);
-    dim3 grid((unsigned)ceil_div(hidden, kTileRows), (unsigned)batch);
-    dim3 block((unsigned)(64 * a.S * a.spr));
-    hipStream_t s = static_cast<hipStream_t>(stream);
     tt_status st;
-    switch (upw * 2 + (h_dtype == TT_F32)) {
-        case 8: st = launch_down<4, false>(a, grid, block, lds, s); break;
-        case 9: st = launch_down<4, true>(a, grid, block, lds, s); break;
-        case 16: st = launch_down<8, false>(a, grid, block, lds, s); break;
-        case 17: st = launch_down<8, true>(a, grid, block, lds, s); break;
-        case 24: st = launch_down<12, false>(a, grid, block, lds, s); break;
-        case 25: st = launch_down<12, true>(a, grid, block, lds, s); break;
-        case 32: st = launch_down<16, false>(a, grid, block, lds, s); break;
-        default: st = launch_down<16, true>(a, grid, block, lds, s); break;
-    }
+    st = upw == 4 ? launch_down<4>(a, grid, block, lds, s) : launch_down<8>(a, grid, block, lds, s);
     if (st == TT_OK) clear_error();
     return st;
 }

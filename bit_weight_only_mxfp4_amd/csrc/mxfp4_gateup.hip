@@ -7,20 +7,19 @@
 // stardance page, "numerical drift & speedups": the same over the selected
 // experts):  out[r] = silu(ps_g[r] * (Wg x)[r]) * (ps_u[r] * (Wu x)[r]).
 //
-// Batch 1 (and the routed experts, one token per slot) runs on the vector
-// ALUs: one workgroup per 16-row tile (8 gate + 8 up rows of the same output
-// features), KS waves splitting the tile's K units.  Per unit a lane streams
-// 16 code bytes (one 32-element block), converts byte pairs of codes to bf16
-// with the hardware FP4 conversion, takes fp32 dot2 products against the
-// activations staged once in LDS, and scales the block's partial sum by its
-// E8M0 scale.  A cross-lane reduction over the 4 pieces of a row and a
-// fixed-order cross-wave sum give the row dot products; the postscale and
-// SwiGLU run in registers.
+// Batch 1 and 2 (and the routed experts, one token per slot) run on the
+// gfx950 scaled matrix instruction: the packed FP4 tile units and their E8M0
+// block scales go to v_mfma_scale_f32_16x16x128_f8f6f4 as they are loaded,
+// against the bf16 activations split into two E4M3 parts with E8M0 scales.
+// One workgroup per 1-2 tiles of 16 rows (8 gate + 8 up rows of the same
+// output features), ks waves splitting the tile's K units; a fixed-order
+// cross-wave sum gives the row dot products, and the postscale and SwiGLU
+// run in registers.
 //
-// Batch 2..32 runs on MFMA (v_mfma_f32_16x16x32_bf16): the same 16-byte loads
-// become bf16 A operands with the block scale folded into the conversion, and
-// each wave keeps the activations of up to 32 tokens over its slice of K in
-// registers as B operands while it streams a run of tiles.
+// Batch 3..32 runs on the bf16 MFMA (v_mfma_f32_16x16x32_bf16): the same
+// 16-byte loads become bf16 A operands with the block scale folded into the
+// conversion, and each wave keeps the activations of up to 32 tokens over its
+// slice of K in registers as B operands while it streams a run of tiles.
 #include <algorithm>
 
 #include "device.h"
@@ -109,22 +108,20 @@ __device__ __forceinline__ int gu_route_topj(uint32_t key[4], int topk, int j, b
     return e;
 }
 
-// Tuning of the vector path: units of K per wave (4, 8, 12 or 16) and tiles
-// per workgroup.
+// Tuning of the scaled-MFMA path: units of K per wave (4 or 8) and tiles per
+// workgroup.
 #ifndef TT_GATEUP_UPW
 #define TT_GATEUP_UPW 4
 #endif
 #ifndef TT_GATEUP_TPB
 #define TT_GATEUP_TPB 2
 #endif
-// Batch 1 and the routed slots on the scaled MFMA (1) or the vector ALUs (0).
-#ifndef TT_GATEUP_MX
-#define TT_GATEUP_MX 1
+// Largest dense batch on the scaled-MFMA path (2 tokens per workgroup).
+#ifndef TT_GATEUP_MX_MAXB
+#define TT_GATEUP_MX_MAXB 2
 #endif
-#ifndef TT_GATEUP_MAXW
-#define TT_GATEUP_MAXW 8
-#endif
-constexpr int kMaxWavesPerTile = TT_GATEUP_MAXW;
+constexpr size_t kMaxLdsBytes = 160 * 1024;
+constexpr int kMaxWavesPerTile = 16;
 constexpr int kPF = 8;           // units in flight per wave (MFMA path)
 constexpr int kOob = 0x7FFFFF00; // buffer offset past every tile: loads return 0
 
@@ -155,210 +152,11 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Vector path.  Workgroup = TPB tiles x ks waves; wave (t, p) owns units
-// [p * UPW, p * UPW + UPW) of tile blockIdx.x * TPB + t.  Issue order per
-// wave: its share of the activations, then all UPW weight loads and UPW / 4
-// scale dwords.  Loads complete in order, so the activations reach LDS while
-// the weights are still streaming; after an LDS-only barrier each unit is
-// consumed as soon as its load lands.  Units past the end of K, and tiles
-// past the end of the pack, read at an out-of-range buffer offset and get
-// zeros, which contribute exactly nothing.
-template <int UPW, int TPB>
-__global__ __launch_bounds__(1024) void k_gateup_valu(GateUpArgs a) {
-    static_assert(UPW % 4 == 0 && UPW <= 16, "units per wave");
-    extern __shared__ __align__(16) uint8_t smem[];
-    const int ks = a.ks;
-    // activations are staged zero-filled up to ks * UPW units, so that the
-    // units past the end of K (zero codes) meet zero activations, never
-    // uninitialised LDS
-    const int xchunks = ks * UPW * 16;
-    uint4 *xs4 = reinterpret_cast<uint4 *>(smem);
-    float *red = reinterpret_cast<float *>(smem + xchunks * 16);
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int nthreads = blockDim.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int tsub = wave / ks, part = wave - tsub * ks;
-    const int tile = blockIdx.x * TPB + tsub, slot = blockIdx.y;
-
-    // routed calls have batch * topk slots; the dense call has one per token
-    const int tok = (a.ids || a.logits) ? slot / a.topk : slot;
-    // 1. activations: each thread fetches at most UPW / 4 chunks of 16 bytes
-    constexpr int XC = UPW / 4;  // nthreads * XC >= xchunks
-    const int xvalid = a.hidden / 8;
-    const uint4 *xg = reinterpret_cast<const uint4 *>(a.x + (int64_t)tok * a.hidden);
-    uint4 xv[XC];
-#pragma unroll
-    for (int j = 0; j < XC; ++j) {
-        const int idx = tid + j * nthreads;
-        xv[j] = idx < xvalid ? xg[idx] : make_uint4(0, 0, 0, 0);
-    }
-
-    // the expert id (routed call) is read after the activation loads are out
-    const uint8_t *base = a.w;
-    if (a.logits) {
-        // fused routing: slot j's expert from the token's logits; the
-        // workgroups of tile 0 also produce the routing outputs
-        const uint16_t *lb = a.logits + (int64_t)tok * a.n_experts;
-        uint32_t key[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ei = lane + 64 * i;
-            key[i] = 0u;
-            if (64 * i < a.n_experts) {  // uniform
-                const uint32_t raw = lb[min(ei, a.n_experts - 1)];
-                key[i] = ei < a.n_experts ? gu_route_key(raw, ei) : 0u;
-            }
-        }
-        float wj = 0.0f;
-        const int j = slot - tok * a.topk;
-        const bool writer = blockIdx.x == 0;
-        const int e = gu_route_topj(key, a.topk, j, writer, &wj);
-        if (writer && tid == 0) {
-            a.ids_out[slot] = e;
-            a.w_out[slot] = wj;
-        }
-        base += (int64_t)e * a.expert_stride;
-    } else if (a.ids) {
-        const int e = a.ids[slot];
-        if (e < 0 || e >= a.n_experts) {
-            for (int i = tid; i < TPB * 8; i += nthreads) {
-                const int pair = blockIdx.x * TPB * 8 + i;
-                if (pair < a.inter)
-                    store_out(a.out, (int64_t)slot * a.inter + pair, __builtin_nanf(""),
-                              a.out_bf16);
-            }
-            return;
-        }
-        base += (int64_t)e * a.expert_stride;
-    }
-
-    // 2. weights
-    const bool tile_ok = tile < a.ntiles;
-    const uint8_t *tb = base + (int64_t)(tile_ok ? tile : 0) * a.tile_stride;
-    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(tb, a.tile_stride);
-    const int q = lane >> 4;
-    const int u0 = part * UPW;
-    const int n = tile_ok ? max(0, min(UPW, a.units - u0)) : 0;
-    uint4 c[UPW];
-    uint32_t sd[UPW / 4];
-    const int voff = u0 * kUnitBytes + lane * 16;
-    const int soff = a.scale_off + (u0 >> 2) * kGroupBytes + lane * 4;
-    // each scale dword goes out just ahead of its four units, so that unit i
-    // only waits for the loads issued before it
-#pragma unroll
-    for (int g = 0; g < UPW / 4; ++g) {
-        sd[g] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * g < n ? soff + g * kGroupBytes : kOob,
-                                                     0, 0);
-#pragma unroll
-        for (int i = 4 * g; i < 4 * g + 4; ++i)
-            c[i] = load16(rs, i < n ? voff + i * kUnitBytes : kOob);
-    }
-    // the row postscales (lanes 0..15 of the wave that finishes the tile) are
-    // fetched with the weights, not after the reduction, so the epilogue adds
-    // no dependent memory round trip
-    const float ps = __builtin_bit_cast(
-        float, __builtin_amdgcn_raw_buffer_load_b32(
-                   rs, (part == 0 && lane < 16 && tile_ok) ? a.ps_off + lane * 4 : kOob, 0, 0));
-
-    // 3. activations to LDS (zero past K), then an LDS-only barrier
-#pragma unroll
-    for (int j = 0; j < XC; ++j) {
-        const int idx = tid + j * nthreads;
-        if (idx < xchunks) xs4[idx] = xv[j];
-    }
-    lds_barrier();
-
-    // 4. consume the units in load order
-    float acc = 0.0f;
-    const uint4 *xb = xs4 + (4 * u0 + q) * 4;
-#pragma unroll
-    for (int i = 0; i < UPW; ++i) {
-        const float p = fp4x32_dot_bf16(c[i], xb + i * 16);
-        const uint32_t e = (sd[i >> 2] >> (8 * (i & 3))) & 255u;
-        acc = fmaf(p, e8m0_f32(e), acc);
-    }
-    // the four pieces of each row -> full row partial (lanes r, r+16, r+32, r+48)
-    acc = sum_xor32(sum_xor16(acc));
-    if (TPB * ks > 1) {
-        if (lane < 16) red[wave * 16 + lane] = acc;
-        lds_barrier();
-        if (part != 0) return;
-        if (lane < 16) {
-            acc = red[(tsub * ks) * 16 + lane];
-            for (int w = 1; w < ks; ++w) acc += red[(tsub * ks + w) * 16 + lane];
-        }
-    }
-    if (!tile_ok) return;
-    const float y = acc * ps;             // tile rows 0..7 gate, 8..15 up
-    // lane r < 8 takes lane r + 8 (DPP row shift left by 8)
-    const float u = __builtin_bit_cast(
-        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, y), 0x108, 0xF, 0xF, false));
-    const int pair = tile * 8 + lane;
-    if (lane < 8 && pair < a.inter)
-        store_out(a.out, (int64_t)slot * a.inter + pair, silu(y) * u, a.out_bf16);
-}
-
-// Scaled-MFMA path (batch 1 and the routed slots).  The gfx950 instruction
-// v_mfma_scale_f32_16x16x128_f8f6f4 multiplies 16 x 128 FP4 (E2M1) weights
-// by 128 x 16 FP8 (E4M3) activations, each 32-element block of either side
-// multiplied by its own E8M0 scale, and accumulates in fp32.  A packed tile
-// unit is its A operand as loaded: lane l holds row l % 16, elements
-// 32 (l / 16) .. +31, and the lane's scale dword holds the E8M0 bytes of
-// that piece for four consecutive units (the byte select of the instruction
-// picks one), so the weights go to the matrix core with no conversion at all.
-// B operand (measured on the device): lane (column c, group g) holds elements
-// 16g .. 16g+15 of the unit in its first four registers and 64+16g .. +15 in
-// the next four; its scale applies to elements 32g .. 32g+31.
-// The bf16 activations are split per 32-element block into two E4M3 parts,
-//   x = 2^(E-7) hi + 2^(E-11) lo,   E = the block's largest bf16 exponent,
-// which holds exactly for every element of magnitude >= 2^(E-13) (hi carries
-// the top 4 significant bits of the 8, lo the rest) and to within 2^(E-21)
-// below that.  Token t's hi part is column t and its lo part column 8 + t;
-// column 8 + t is added onto column t after the last unit.
-typedef __attribute__((ext_vector_type(8))) int i32x8_t;
-
-// Largest bf16 exponent field among the 8 elements of a 16-byte chunk.
-__device__ __forceinline__ uint32_t bf16x8_max_exp(uint4 v) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) m = max(m, max((w[i] >> 7) & 255u, (w[i] >> 23) & 255u));
-    return m;
-}
-
-// hi and lo E4M3 parts of 4 bf16 values (2 dwords) times mult = 2^(127 - sh).
-__device__ __forceinline__ void split4(uint32_t w0, uint32_t w1, float mult, uint32_t *hi,
-                                       uint32_t *lo) {
-    const float v0 = bf16_bits_to_f32(w0 & 0xFFFFu) * mult, v1 = bf16_bits_to_f32(w0 >> 16) * mult;
-    const float v2 = bf16_bits_to_f32(w1 & 0xFFFFu) * mult, v3 = bf16_bits_to_f32(w1 >> 16) * mult;
-    int h = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
-    h = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, h, true);
-    const f32x2_t b01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
-    const f32x2_t b23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
-    int l = __builtin_amdgcn_cvt_pk_fp8_f32((v0 - b01.x) * 16.0f, (v1 - b01.y) * 16.0f, 0, false);
-    l = __builtin_amdgcn_cvt_pk_fp8_f32((v2 - b23.x) * 16.0f, (v3 - b23.y) * 16.0f, l, true);
-    *hi = (uint32_t)h;
-    *lo = (uint32_t)l;
-}
-
-// One scaled MFMA, FP4 A by FP8 B; byte sel of both scale dwords (the
-// selector must be a constant: the unrolled unit index folds the switch).
-template <int SEL>
-__device__ __forceinline__ f32x4_t mfma_fp4_fp8_sel(i32x8_t A, i32x8_t B, f32x4_t C, uint32_t sa,
-                                                    uint32_t sb) {
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, C, 4, 0, SEL, (int)sa, SEL,
-                                                            (int)sb);
-}
-__device__ __forceinline__ f32x4_t mfma_fp4_fp8(int sel, i32x8_t A, i32x8_t B, f32x4_t C,
-                                                uint32_t sa, uint32_t sb) {
-    switch (sel) {
-        case 0: return mfma_fp4_fp8_sel<0>(A, B, C, sa, sb);
-        case 1: return mfma_fp4_fp8_sel<1>(A, B, C, sa, sb);
-        case 2: return mfma_fp4_fp8_sel<2>(A, B, C, sa, sb);
-        default: return mfma_fp4_fp8_sel<3>(A, B, C, sa, sb);
-    }
-}
-
+// Scaled-MFMA path (batch 1 and 2 and the routed slots): each packed unit
+// and its E8M0 scale byte go to v_mfma_scale_f32_16x16x128_f8f6f4 as loaded
+// (layouts and the two-part E4M3 activations: device.h).  Token t's hi part
+// is B column t and its lo part column 8 + t; column 8 + t is added onto
+// column t after the last unit.
 template <int NTOK>
 struct MxLds {
     int kp;  // staged elements per token (a multiple of 512)
@@ -381,7 +179,7 @@ __host__ __device__ constexpr size_t mx_lds_bytes(int ks, int upw, int tpb) {
 }
 
 // Workgroup = TPB tiles x ks waves, wave (t, p) owns units [p UPW, p UPW +
-// UPW) of tile blockIdx.x * TPB + t, as on the vector path.  NTOK tokens per
+// UPW) of tile blockIdx.x * TPB + t.  NTOK tokens per
 // workgroup (dense calls: tokens blockIdx.y * NTOK ..; routed calls: NTOK = 1,
 // slot blockIdx.y).  Issue order per wave: its share of the activations,
 // then each scale dword followed by its four units, then the postscales;
@@ -481,25 +279,15 @@ __global__ __launch_bounds__(1024) void k_gateup_mx(GateUpArgs a) {
     // keep every load above the activation split
     __builtin_amdgcn_sched_barrier(0);
 
-    // 3. activations -> E4M3 parts and their scales in LDS.  The four chunks
-    //    of a 32-element block sit in four consecutive lanes; their largest
-    //    exponent is shared through two DPP quad swaps.
+    // 3. activations -> E4M3 parts and their scales in LDS
 #pragma unroll
     for (int j = 0; j < XC; ++j) {
         const int idx = tid + j * nthreads, t = idx / tchunks, ci = idx - t * tchunks;
-        uint32_t e = bf16x8_max_exp(xv[j]);
-        e = max(e, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)e, 0xB1, 0xF, 0xF, false));
-        e = max(e, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)e, 0x4E, 0xF, 0xF, false));
+        uint2 hi, lo;
+        const uint32_t sh = split_chunk(xv[j], &hi, &lo);
         if (t < NTOK) {
-            // scale byte of the hi part: 2^(E-7) with E = e - 127, kept in
-            // [5, 254] (the lo part's byte is 4 less)
-            const uint32_t sh = min(max(e, 12u) - 7u, 254u);
-            const float mult = __builtin_bit_cast(float, (254u - sh) << 23);
-            uint32_t h0, h1, l0, l1;
-            split4(xv[j].x, xv[j].y, mult, &h0, &l0);
-            split4(xv[j].z, xv[j].w, mult, &h1, &l1);
-            *reinterpret_cast<uint2 *>(smem + L.q_off(t, 0) + ci * 8) = make_uint2(h0, h1);
-            *reinterpret_cast<uint2 *>(smem + L.q_off(t, 1) + ci * 8) = make_uint2(l0, l1);
+            *reinterpret_cast<uint2 *>(smem + L.q_off(t, 0) + ci * 8) = hi;
+            *reinterpret_cast<uint2 *>(smem + L.q_off(t, 1) + ci * 8) = lo;
             if ((ci & 3) == 0) {
                 const int blk = ci >> 2;
                 smem[L.s_off(t, 0, blk & 3, blk >> 2)] = (uint8_t)sh;
@@ -721,16 +509,21 @@ int device_cus() {
     return cus[dev];
 }
 
-template <int UPW>
-tt_status launch_valu_upw(GateUpArgs a, int slots, int tpb_max, hipStream_t stream) {
-    a.ks = (int32_t)ceil_div(a.units, UPW);
-    const int tpb = (a.ks * TT_GATEUP_TPB <= 8 && tpb_max >= TT_GATEUP_TPB) ? TT_GATEUP_TPB : 1;
-    const size_t lds = (size_t)a.ks * UPW * 256 + (size_t)tpb * a.ks * 64;
-    dim3 grid((unsigned)ceil_div(a.ntiles, tpb), (unsigned)slots);
-    const char *what = "mxfp4 gate/up (vector path)";
-    if (tpb == 1)
-        return launch(what, k_gateup_valu<UPW, 1>, grid, dim3(64 * a.ks), lds, stream, a);
-    return launch(what, k_gateup_valu<UPW, TT_GATEUP_TPB>, grid, dim3(64 * tpb * a.ks), lds,
+template <int UPW, int TPB, int NTOK>
+tt_status launch_mx(const GateUpArgs &a, dim3 grid, dim3 block, size_t lds, hipStream_t stream) {
+    if (lds > 64 * 1024) {
+        static bool raised[64] = {false};
+        int dev = 0;
+        (void)hipGetDevice(&dev);
+        if (dev >= 0 && dev < 64 && !raised[dev]) {
+            if (hipFuncSetAttribute(reinterpret_cast<const void *>(k_gateup_mx<UPW, TPB, NTOK>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)kMaxLdsBytes) != hipSuccess)
+                return fail(TT_E_HIP, "cannot raise the LDS limit of the gate/up kernel");
+            raised[dev] = true;
+        }
+    }
+    return launch("mxfp4 gate/up (scaled MFMA)", k_gateup_mx<UPW, TPB, NTOK>, grid, block, lds,
                   stream, a);
 }
 
@@ -739,25 +532,34 @@ tt_status launch_mx_upw(GateUpArgs a, int slots, int tpb_max, hipStream_t stream
     a.ks = (int32_t)ceil_div(a.units, UPW);
     const int tpb = (a.ks * TT_GATEUP_TPB <= 8 && tpb_max >= TT_GATEUP_TPB) ? TT_GATEUP_TPB : 1;
     const size_t lds = mx_lds_bytes<NTOK>(a.ks, UPW, tpb);
+    if (lds > kMaxLdsBytes)
+        return fail(TT_E_SHAPE, "hidden = %d with %d tokens: the staged activations do not fit "
+                    "in LDS", a.hidden, NTOK);
     dim3 grid((unsigned)ceil_div(a.ntiles, tpb), (unsigned)slots);
-    const char *what = "mxfp4 gate/up (scaled MFMA)";
-    if (tpb == 1)
-        return launch(what, k_gateup_mx<UPW, 1, NTOK>, grid, dim3(64 * a.ks), lds, stream, a);
-    return launch(what, k_gateup_mx<UPW, TT_GATEUP_TPB, NTOK>, grid, dim3(64 * tpb * a.ks), lds,
-                  stream, a);
+    if (tpb == 1) return launch_mx<UPW, 1, NTOK>(a, grid, dim3(64 * a.ks), lds, stream);
+    return launch_mx<UPW, TT_GATEUP_TPB, NTOK>(a, grid, dim3(64 * tpb * a.ks), lds, stream);
 }
 
-// Units per wave: the tuned target, raised until a tile needs at most
-// kMaxWavesPerTile waves (16 on the scaled-MFMA path, K <= 16384 gives at
-// most 128 units, so 8 units per wave always suffice; 8 on the vector path).
-// A grid of 4-unit waves that overflows what the chip holds at once (7-8
-// waves per SIMD at these register counts) but fits it with 8-unit waves in
-// one-tile workgroups switches to those: the routed calls, batch x topk
-// slots of every tile, would otherwise run a second, partial round.
-tt_status launch_valu(GateUpArgs a, int slots, hipStream_t stream) {
-    const int maxw = TT_GATEUP_MX ? 16 : kMaxWavesPerTile;
+// One or two tokens per workgroup (the routed calls take one).  Every
+// workgroup splits the activations of all its tokens over the whole K, so
+// that work grows with the batch: at 4 tokens the bf16 MFMA path is as fast,
+// at 8 it is clearly faster (measured on SmolLM3-sized layers).
+template <int UPW>
+tt_status launch_mx_ntok(const GateUpArgs &a, int slots, int dense_batch, int tpb_max,
+                         hipStream_t stream) {
+    if (dense_batch <= 1) return launch_mx_upw<UPW, 1>(a, slots, tpb_max, stream);
+    return launch_mx_upw<UPW, 2>(a, (int)ceil_div(dense_batch, 2), tpb_max, stream);
+}
+
+// Units per wave: the tuned target, raised until a tile needs at most 16
+// waves (K <= 16384 gives at most 128 units, so 8 units per wave always
+// suffice).  A grid of 4-unit waves that overflows what the chip holds at
+// once (7-8 waves per SIMD at these register counts) but fits it with 8-unit
+// waves in one-tile workgroups switches to those: the routed calls, batch x
+// topk slots of every tile, would otherwise run a second, partial round.
+tt_status launch_scaled(GateUpArgs a, int slots, hipStream_t stream, int dense_batch = 1) {
     int upw = TT_GATEUP_UPW;
-    while (ceil_div(a.units, upw) > maxw) upw += 4;
+    while (ceil_div(a.units, upw) > kMaxWavesPerTile) upw += 4;
     int tpb_max = TT_GATEUP_TPB;
     const int64_t resident = (int64_t)device_cus() * 4 * 7;
     if (upw == 4 && (int64_t)slots * a.ntiles * ceil_div(a.units, 4) > resident &&
@@ -765,21 +567,11 @@ tt_status launch_valu(GateUpArgs a, int slots, hipStream_t stream) {
         upw = 8;
         tpb_max = 1;
     }
-#if TT_GATEUP_MX
     switch (upw) {
-        case 4: return launch_mx_upw<4, 1>(a, slots, tpb_max, stream);
-        case 8: return launch_mx_upw<8, 1>(a, slots, tpb_max, stream);
+        case 4: return launch_mx_ntok<4>(a, slots, dense_batch, tpb_max, stream);
+        case 8: return launch_mx_ntok<8>(a, slots, dense_batch, tpb_max, stream);
         default: return fail(TT_E_SHAPE, "hidden = %d needs more than 16 waves per tile", a.hidden);
     }
-#else
-    switch (upw) {
-        case 4: return launch_valu_upw<4>(a, slots, tpb_max, stream);
-        case 8: return launch_valu_upw<8>(a, slots, tpb_max, stream);
-        case 12: return launch_valu_upw<12>(a, slots, tpb_max, stream);
-        case 16: return launch_valu_upw<16>(a, slots, tpb_max, stream);
-        default: return fail(TT_E_SHAPE, "hidden = %d needs more than 8 waves per tile", a.hidden);
-    }
-#endif
 }
 
 constexpr size_t kMaxLds = 160 * 1024;
@@ -873,7 +665,9 @@ extern "C" tt_status tt_mxfp4_gateup_swiglu(const void *w_gu, int64_t inter, int
     hipStream_t s = static_cast<hipStream_t>(stream);
     tt_status st;
     if (batch == 1)
-        st = launch_valu(a, 1, s);
+        st = launch_scaled(a, 1, s);
+    else if (batch <= TT_GATEUP_MX_MAXB)
+        st = launch_scaled(a, 1, s, (int)batch);
     else if (batch <= 16)
         st = launch_mfma<1>(a, s);
     else
@@ -895,7 +689,7 @@ extern "C" tt_status tt_moe_mxfp4_gateup_swiglu(const void *bank, int64_t n_expe
     a.ids = ids;
     a.topk = (int32_t)topk;
     a.n_experts = (int32_t)n_experts;
-    tt_status st = launch_valu(a, (int)(batch * topk), static_cast<hipStream_t>(stream));
+    tt_status st = launch_scaled(a, (int)(batch * topk), static_cast<hipStream_t>(stream));
     if (st == TT_OK) clear_error();
     return st;
 }
@@ -921,7 +715,7 @@ extern "C" tt_status tt_moe_mxfp4_route_gateup_swiglu(const void *bank, int64_t 
     a.logits = static_cast<const uint16_t *>(logits);
     a.ids_out = ids;
     a.w_out = w;
-    tt_status st = launch_valu(a, (int)(batch * topk), static_cast<hipStream_t>(stream));
+    tt_status st = launch_scaled(a, (int)(batch * topk), static_cast<hipStream_t>(stream));
     if (st == TT_OK) clear_error();
     return st;
 }
