@@ -169,6 +169,26 @@ def test_moe_down_ragged(dev, hidden, inter, topk, h_bf16):
     assert_parity(to_np(y), yr, gemv_tol(S, yr), f"moe down h{hidden} i{inter} k{topk}")
 
 
+def test_moe_down_wide_range_bf16_h(dev):
+    """bf16 h spread over 2^52 within every block (the two-part E4M3 split of
+    the scaled-MFMA down kernel): parity at the usual bar."""
+    n_exp, topk = 6, 4
+    w = workloads.Workload(9, "widedn", 512, 2880, n_experts=n_exp, topk=topk)
+    db = workloads.expert_bank(w, 0, "down")
+    dn = dev_u8(_down_pack(db, n_exp, w.hidden, w.inter), dev)
+    gen = np.random.default_rng(515)
+    mag = np.exp2(gen.uniform(-40, 12, (1, topk, w.inter)))
+    h = (np.where(gen.random(mag.shape) < 0.5, -1.0, 1.0) * mag).astype(np.float32)
+    h = workloads.bf16_to_f32(workloads.bf16_bits(h))
+    ids = np.array([[0, 5, 2, 3]], np.int32)
+    wt = gen.uniform(0.05, 1.0, (1, topk)).astype(np.float32)
+    y = tt.moe_mxfp4_down_combine(dn, n_exp, w.hidden, w.inter,
+                                  torch.from_numpy(h).to(dev).to(torch.bfloat16),
+                                  torch.from_numpy(ids).to(dev), torch.from_numpy(wt).to(dev))
+    yr, S = oracle.moe_down_combine(db, n_exp, w.hidden, w.inter, h, ids, wt.astype(np.float64))
+    assert_parity(to_np(y), yr, gemv_tol(S, yr), "moe down wide-range bf16 h")
+
+
 # ---- INT4 ----------------------------------------------------------------------
 
 def _int4_case(dev, n, k, batch, layer=0, tensor=workloads.T_INT4W):

@@ -221,3 +221,47 @@ def test_quantized_fp32_weights_end_to_end(dev, batch):
     e_fit = ((wg - ps[:, None] * d) ** 2).sum(axis=1)
     e_one = ((wg - d) ** 2).sum(axis=1)
     assert np.all(e_fit <= e_one * (1 + 1e-12))
+
+
+def _wide_range_bf16(gen, shape, lo=-40, hi=12):
+    """bf16 activations with magnitudes 2^U(lo, hi) and random signs: every
+    32-element block spans far more than the 2^13 its two E4M3 parts carry
+    exactly, so the small elements exercise the lo part's rounding, and zeros
+    and exact powers of two are mixed in."""
+    mag = np.exp2(gen.uniform(lo, hi, shape))
+    sign = np.where(gen.random(shape) < 0.5, -1.0, 1.0)
+    x = (sign * mag).astype(np.float32)
+    x[gen.random(shape) < 0.05] = 0.0
+    pw = gen.random(shape) < 0.05
+    x[pw] = np.exp2(np.round(gen.uniform(lo, hi, int(pw.sum())))).astype(np.float32)
+    return workloads.bf16_bits(x)
+
+
+@pytest.mark.parametrize("batch", [1, 2])
+def test_wide_range_activations(dev, batch):
+    """Activations spread over 2^52 within every block, through the two-part
+    E4M3 split of the scaled-MFMA path: parity at the usual bar."""
+    w = workloads.Workload(9, "wide", 2048, 640)
+    x = _wide_range_bf16(np.random.default_rng(77 + batch), (batch, w.hidden))
+    got, ref = _gateup_case(dev, w, 0, batch, x=x)
+    assert_parity(got, ref["h"], h_tol(ref), f"wide-range x b{batch}")
+
+
+def test_block_exponent_extremes(dev):
+    """Blocks whose largest element sits at the top and at the bottom of the
+    bf16 normal range (the split's scale byte clamps) and an all-zero block:
+    parity at the usual bar, no overflow or NaN."""
+    w = workloads.Workload(9, "ext", 256, 128)
+    x = np.zeros((1, w.hidden), np.float32)
+    x[0, 0:32] = np.float32(2.0 ** 120) * np.linspace(-1, 1, 32, dtype=np.float32)
+    x[0, 32:64] = np.float32(2.0 ** -120) * np.linspace(1, 2, 32, dtype=np.float32)
+    x[0, 96:128] = np.float32(3.0) * np.float32(2.0 ** -126)     # smallest normals
+    x[0, 128:160] = np.float32(1.0)
+    # gate/up values near 2^120 would overflow silu * up; scale those columns
+    # to zero weight so the rows stay finite: the test is about the split
+    g, u = workloads.gateup(w)
+    for cu in (g, u):
+        cu[0][:, 0:16] = 0
+    got, ref = _gateup_case(dev, w, 0, 1, g=g, u=u, x=workloads.bf16_bits(x))
+    assert np.all(np.isfinite(got))
+    assert_parity(got, ref["h"], h_tol(ref), "block exponent extremes")
