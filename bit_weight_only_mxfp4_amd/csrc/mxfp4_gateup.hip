@@ -41,8 +41,8 @@ struct GateUpArgs {
     void *out;              // [slots][inter]
     int32_t out_bf16;
     int32_t inter;
-    int32_t batch;          // tokens (MFMA path)
-    int32_t ks;             // waves per tile (vector path)
+    int32_t batch;          // tokens (dense calls)
+    int32_t ks;             // waves per tile (scaled-MFMA path: the K split)
     const uint16_t *logits; // fused routing: bf16 [tokens][n_experts], or NULL
     int32_t *ids_out;       // fused routing: chosen experts [slots]
     float *w_out;           // fused routing: routing weights [slots]
@@ -122,7 +122,6 @@ __device__ __forceinline__ int gu_route_topj(uint32_t key[4], int topk, int j, b
 #endif
 constexpr size_t kMaxLdsBytes = 160 * 1024;
 constexpr int kMaxWavesPerTile = 16;
-constexpr int kPF = 8;           // units in flight per wave (MFMA path)
 constexpr int kOob = 0x7FFFFF00; // buffer offset past every tile: loads return 0
 
 // Byte offset of lane `lane`'s 16 code bytes in unit kk.  Lanes whose piece
@@ -179,12 +178,15 @@ __host__ __device__ constexpr size_t mx_lds_bytes(int ks, int upw, int tpb) {
 }
 
 // Workgroup = TPB tiles x ks waves, wave (t, p) owns units [p UPW, p UPW +
-// UPW) of tile blockIdx.x * TPB + t.  NTOK tokens per
-// workgroup (dense calls: tokens blockIdx.y * NTOK ..; routed calls: NTOK = 1,
-// slot blockIdx.y).  Issue order per wave: its share of the activations,
-// then each scale dword followed by its four units, then the postscales;
-// the activations are split into their E4M3 parts into LDS, and after an
+// UPW) of tile blockIdx.x * TPB + t.  NTOK tokens per workgroup (dense
+// calls: tokens blockIdx.y * NTOK ..; routed calls: NTOK = 1, slot
+// blockIdx.y).  Issue order per wave: its share of the activations, then
+// each scale dword followed by its four units, then the postscales; the
+// activations are split into their E4M3 parts into LDS, and after an
 // LDS-only barrier each unit goes to the matrix core as its load lands.
+// Lanes whose piece of the last unit lies past the row end read whatever
+// follows (FP4 codes have no NaN; the pack gives them scale byte 127) against
+// zero activations, so they add exactly zero; loads past the tile return 0.
 template <int UPW, int TPB, int NTOK>
 __global__ __launch_bounds__(1024) void k_gateup_mx(GateUpArgs a) {
     static_assert(UPW % 4 == 0 && UPW <= 16, "units per wave");
