@@ -403,7 +403,7 @@ def run(args):
         yq = torch.empty((1, nq), dtype=bf, device=dev)
         att = torch.empty((hq, d), dtype=bf, device=dev)
         yo = torch.empty((1, no), dtype=bf, device=dev)
-        h = torch.empty((1, w.inter), device=dev)
+        h = torch.empty((1, w.inter), dtype=bf, device=dev)   # bf16 like every activation
         y = torch.empty((1, w.hidden), device=dev)
 
         def layer_calls(qkv, o4, gu, dn, kc, vc):
@@ -422,8 +422,8 @@ def run(args):
 
         secs = time_steps(torch, step, K, W)
         per_layer = (int4_bytes(nq, kq, 1) - nq * 2 + 2 * hkv * T * d * 2 + hq * d * 2
-                     + int4_bytes(no, ko, 1) - no * 2 + gateup_bytes(w.inter, w.hidden, 1)
-                     + w.hidden * w.inter + w.hidden * 4 + w.inter * 4 + w.hidden * 4)
+                     + int4_bytes(no, ko, 1) - no * 2 + gateup_bytes(w.inter, w.hidden, 1, 2)
+                     + w.hidden * w.inter + w.hidden * 4 + w.inter * 2 + w.hidden * 4)
         gbs = per_layer * layers * K / secs / 1e9
         result = dict(metric="effective HBM GB/s of one dense decode layer run as one HIP graph "
                              "(INT4 QKV, GQA attention, INT4 O, MXFP4 gate/up SwiGLU, FP8 down)",

@@ -16,9 +16,12 @@
 // UPW).  Issue order per wave: its share of the activations (straight-line
 // buffer loads, zeros past k and past the batch), then its UPW code units,
 // then -- in wave 0 -- the tile's row scales.  The activations go to LDS as
-// fp32 (bf16 converts exactly); after an LDS-only barrier each unit is
-// consumed as its load lands: v_cvt_scalef32_pk_f32_fp8 (scale 1) turns two
+// they are; after an LDS-only barrier each unit is consumed as its load
+// lands.  fp32 activations: v_cvt_scalef32_pk_f32_fp8 (scale 1) turns two
 // E4M3 codes into two exact fp32 values, one FMA per element accumulates.
+// bf16 activations: v_cvt_scalef32_pk_bf16_fp8 turns two codes into two exact
+// bf16 values and one dot2 takes the pair (4 instead of 6 VALU ops per 4
+// codes, half the LDS reads).
 // Reduction: xor-shuffles over the 8 pieces of each row, then a fixed-order
 // cross-wave sum in LDS; the row scale multiplies the full sum.
 #include "device.h"
@@ -60,13 +63,25 @@ __device__ __forceinline__ float f8x4_dot(uint32_t c, float4 x, float acc) {
     return fmaf(hi.y, x.w, acc);
 }
 
+// The same against bf16 activations: v_cvt_scalef32_pk_bf16_fp8 turns two
+// codes into two exact bf16 values, and dot2 takes the pair with its two
+// activations (xw0 = x[0], x[1]; xw1 = x[2], x[3]).
+__device__ __forceinline__ float f8x4_dot_bf16(uint32_t c, uint32_t xw0, uint32_t xw1,
+                                               float acc) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, false),
+                                          as_bf16x2(xw0), acc, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, true),
+                                           as_bf16x2(xw1), acc, false);
+}
+
 template <int UPW, int NT, bool XF32>
 __global__ __launch_bounds__(1024) void k_fp8_gemv(F8Args a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int ks = a.ks;
+    constexpr int XSZ = XF32 ? 4 : 2;            // staged bytes per activation
     const int kp = ks * UPW * kF8UnitK;           // staged K per token, zero past k
-    float *xs = reinterpret_cast<float *>(smem);  // [NT][kp]
-    float *red = xs + NT * kp;                    // [ks][NT][8]
+    float *xs = reinterpret_cast<float *>(smem);  // [NT][kp] fp32, or bf16 as uint16
+    float *red = reinterpret_cast<float *>(smem + (size_t)NT * kp * XSZ);  // [ks][NT][8]
     const int tid = threadIdx.x, lane = tid & 63;
     const int nthreads = blockDim.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -103,22 +118,12 @@ __global__ __launch_bounds__(1024) void k_fp8_gemv(F8Args a) {
         float, __builtin_amdgcn_raw_buffer_load_b32(
                    rs, (wave == 0 && lane < kF8TileRows) ? a.scale_off + lane * 4 : kF8Oob, 0, 0));
 
-    // 3. activations to LDS as fp32, then an LDS-only barrier
+    // 3. activations to LDS as they are (fp32 or bf16), then an LDS-only
+    //    barrier
 #pragma unroll
     for (int c = 0; c < XC; ++c) {
         const int idx = tid + c * nthreads;
-        if (idx < NT * chunks) {
-            float4 *dst = reinterpret_cast<float4 *>(xs) + idx * (EPC / 4);
-            if (XF32) {
-                dst[0] = __builtin_bit_cast(float4, xv[c]);
-            } else {
-                const uint32_t w4[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
-                dst[0] = make_float4(bf16_bits_to_f32(w4[0] & 0xFFFFu), bf16_bits_to_f32(w4[0] >> 16),
-                                     bf16_bits_to_f32(w4[1] & 0xFFFFu), bf16_bits_to_f32(w4[1] >> 16));
-                dst[1] = make_float4(bf16_bits_to_f32(w4[2] & 0xFFFFu), bf16_bits_to_f32(w4[2] >> 16),
-                                     bf16_bits_to_f32(w4[3] & 0xFFFFu), bf16_bits_to_f32(w4[3] >> 16));
-            }
-        }
+        if (idx < NT * chunks) reinterpret_cast<uint4 *>(xs)[idx] = xv[c];
     }
     f8_lds_barrier();
 
@@ -131,12 +136,23 @@ __global__ __launch_bounds__(1024) void k_fp8_gemv(F8Args a) {
     for (int i = 0; i < UPW; ++i) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const float4 *xg = reinterpret_cast<const float4 *>(xs + t * kp +
-                                                                kF8UnitK * (u0 + i) + 16 * q);
-            float d0 = f8x4_dot(cu[i].x, xg[0], 0.0f);
-            float d1 = f8x4_dot(cu[i].y, xg[1], 0.0f);
-            d0 = f8x4_dot(cu[i].z, xg[2], d0);
-            d1 = f8x4_dot(cu[i].w, xg[3], d1);
+            float d0, d1;
+            if (XF32) {
+                const float4 *xg = reinterpret_cast<const float4 *>(xs + t * kp +
+                                                                    kF8UnitK * (u0 + i) + 16 * q);
+                d0 = f8x4_dot(cu[i].x, xg[0], 0.0f);
+                d1 = f8x4_dot(cu[i].y, xg[1], 0.0f);
+                d0 = f8x4_dot(cu[i].z, xg[2], d0);
+                d1 = f8x4_dot(cu[i].w, xg[3], d1);
+            } else {
+                const uint4 *xg = reinterpret_cast<const uint4 *>(
+                    reinterpret_cast<const uint16_t *>(xs) + t * kp + kF8UnitK * (u0 + i) + 16 * q);
+                const uint4 xa = xg[0], xb = xg[1];
+                d0 = f8x4_dot_bf16(cu[i].x, xa.x, xa.y, 0.0f);
+                d1 = f8x4_dot_bf16(cu[i].y, xa.z, xa.w, 0.0f);
+                d0 = f8x4_dot_bf16(cu[i].z, xb.x, xb.y, d0);
+                d1 = f8x4_dot_bf16(cu[i].w, xb.z, xb.w, d1);
+            }
             acc[t] += d0 + d1;
         }
     }
@@ -170,14 +186,14 @@ namespace {
 
 constexpr size_t kF8LdsMax = 160 * 1024;
 
-size_t f8_lds(int ks, int upw, int nt) {
-    return (size_t)nt * ks * upw * kF8UnitK * 4 + (size_t)ks * nt * kF8TileRows * 4;
+size_t f8_lds(int ks, int upw, int nt, bool xf32) {
+    return (size_t)nt * ks * upw * kF8UnitK * (xf32 ? 4 : 2) + (size_t)ks * nt * kF8TileRows * 4;
 }
 
 template <int UPW, int NT, bool XF32>
 tt_status launch_f8(F8Args a, hipStream_t s) {
     a.ks = (int32_t)ceil_div(a.units, UPW);
-    const size_t lds = f8_lds(a.ks, UPW, NT);
+    const size_t lds = f8_lds(a.ks, UPW, NT, XF32);
     auto kern = k_fp8_gemv<UPW, NT, XF32>;
     if (lds > 64 * 1024) {
         static bool raised[64] = {false};
@@ -207,7 +223,7 @@ tt_status launch_f8_nt(const F8Args &a, hipStream_t s) {
     // registers allow
     const int ks = (int)ceil_div(a.units, UPW);
     int nt = a.batch == 1 ? 1 : a.batch == 2 ? 2 : 4;
-    while (nt > 1 && (f8_lds(ks, UPW, nt) > kF8LdsMax || !f8_fits(UPW, nt, XF32))) nt /= 2;
+    while (nt > 1 && (f8_lds(ks, UPW, nt, XF32) > kF8LdsMax || !f8_fits(UPW, nt, XF32))) nt /= 2;
     if constexpr (f8_fits(UPW, 4, XF32))
         if (nt == 4) return launch_f8<UPW, 4, XF32>(a, s);
     if constexpr (f8_fits(UPW, 2, XF32))
