@@ -218,7 +218,7 @@ __global__ __launch_bounds__(1024) void k_down_combine(DownArgs a) {
     for (int jj = 0; jj < topk; ++jj) {
         float dot = red[(jj * S) * 16 + lane];
         for (int pp = 1; pp < S; ++pp) dot += red[(jj * S + pp) * 16 + lane];
-        y += pss[jj * 17 + 16] * (pss[jj * 17 + lane] * dot);
+        y = fmaf(pss[jj * 17 + 16], pss[jj * 17 + lane] * dot, y);  // w_j (ps dot), one rounding
     }
     const int row = tile * 16 + lane;
     if (row < a.hidden) store_out(a.y, (int64_t)b * a.hidden + row, y, a.y_bf16);
@@ -353,7 +353,7 @@ __global__ __launch_bounds__(1024) void k_down_mx(DownArgs a) {
     for (int jj = 0; jj < topk; ++jj) {
         float dot = red[(jj * S) * 16 + lane];
         for (int pp = 1; pp < S; ++pp) dot += red[(jj * S + pp) * 16 + lane];
-        y += pss[jj * 17 + 16] * (pss[jj * 17 + lane] * dot);
+        y = fmaf(pss[jj * 17 + 16], pss[jj * 17 + lane] * dot, y);  // w_j (ps dot), one rounding
     }
     const int row = tile * 16 + lane;
     if (row < a.hidden) store_out(a.y, (int64_t)b * a.hidden + row, y, a.y_bf16);
