@@ -329,9 +329,11 @@ def run(args):
                                         "fp8_down_smollm3.md")))
 
     elif args.workload == "attention":
-        # single-token GQA attention, Phi-4-shaped heads (40 query / 10 kv x
-        # 128), a 4096-position bf16 KV cache per layer, 24 layers rotated
-        hq, hkv, d, T, layers = 40, 10, 128, args.context, 24
+        # single-token GQA attention, Phi-4-shaped heads by default (40 query /
+        # 10 kv x 128; --heads), a 4096-position bf16 KV cache per layer, 24
+        # layers rotated
+        hq, hkv, d = (int(v) for v in args.heads.split(","))
+        T, layers = args.context, 24
         log(f"setup attention hq {hq} hkv {hkv} d {d} T {T}, {layers} layers")
         gen = np.random.default_rng([0, 77])
         caches = []
@@ -361,7 +363,9 @@ def run(args):
                              "cache",
                       value=round(gbs, 2), unit="GB/s", us_per_call=round(secs / calls * 1e6, 3),
                       ms_per_step=round(secs / K * 1e3, 4), bytes_per_call=per_call,
-                      config=dict(workload=f"phi4-14b-gqa-attention-40-10x128-T{T}", hq=hq,
+                      config=dict(workload=(f"phi4-14b-gqa-attention-40-10x128-T{T}"
+                                            if (hq, hkv, d) == (40, 10, 128) else
+                                            f"gqa-attention-{hq}-{hkv}x{d}-T{T}"), hq=hq,
                                   hkv=hkv, d=d, T=T, layers_rotated=layers,
                                   launch="one HIP graph per step (2 kernels per call)"),
                       roofline=dict(bound="hbm", kernel="k_attn_partial+k_attn_combine",
@@ -369,7 +373,8 @@ def run(args):
                                     frac=round(gbs / PEAK_HBM_GBS, 4),
                                     traffic=profiled_traffic(
                                         ("attention.hip", "device.h"),
-                                        "attention_phi4_t4096.md") if T == 4096 else None))
+                                        "attention_phi4_t4096.md")
+                                    if (T, hq, hkv, d) == (4096, 40, 10, 128) else None))
 
     elif args.workload == "phi4-layer":
         # one dense decode layer as one HIP graph, Phi-4 shapes: INT4 QKV ->
@@ -515,6 +520,9 @@ def main():
     ap.add_argument("--batch", type=int, default=8)
     ap.add_argument("--context", type=int, default=4096,
                     help="cached positions for --workload attention")
+    ap.add_argument("--heads", default="40,10,128",
+                    help="query heads, kv heads, head dim for --workload attention "
+                         "(default Phi-4; gpt-oss-20b: 64,8,64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
