@@ -5,34 +5,24 @@
 // values over the cached positions).
 //
 // Split over positions (flash-decoding style), two kernels:
-//  1. k_attn_partial, one workgroup of 4 waves per (64-position chunk, kv
-//     head): every wave issues its query slices, then the key rows and value
-//     rows of its 16 positions (straight-line buffer loads; positions past T
-//     read zeros and score -inf), scores the G query heads of the kv head
-//     with dot2 on bf16 pairs, takes the chunk's per-head maximum across the
-//     waves, and accumulates p = exp(s - max) and p * V in fp32 (scores are
-//     kept in base-2 units, s * log2(e), so each exponential is one
-//     v_exp_f32).  The chunk's (max, sum p, sum p V) per head go to the
-//     caller's workspace.
-//  2. k_attn_combine, one workgroup per query head: rescales the chunks to
-//     the global maximum and sums them in chunk order (fixed order: the
-//     result is the same on every run).
-// Lane mapping: a key/value row of D bf16 is D / 8 lanes x 16 bytes; a wave
-// load covers 64 / (D / 8) positions.
+//  1. k_attn_partial, one wave per (64-position chunk, kv head): the G query
+//     heads of the kv head against the chunk's keys and values on the bf16
+//     matrix cores (scores K Q^T, then P V), scores in base-2 units
+//     (s * scale * log2(e), so each exponential is one v_exp_f32), positions
+//     past T read zeros and score -inf.  The chunk's (max, sum p, sum p V)
+//     per head go to the caller's workspace.
+//  2. k_attn_combine, one wave per (query head, 64 output columns): rescales
+//     the chunks to the global maximum and sums them in chunk order (fixed
+//     order: the result is the same on every run).
 #include "device.h"
 #include "tt_internal.h"
 
 namespace tt {
 
-#ifndef TT_ATTN_WAVES
-#define TT_ATTN_WAVES 4
-#endif
 #ifndef TT_ATTN_CHUNK
 #define TT_ATTN_CHUNK 64
 #endif
-constexpr int kAttnWaves = TT_ATTN_WAVES;
-constexpr int kAttnChunk = TT_ATTN_CHUNK;  // positions per workgroup
-constexpr int kAttnPerWave = kAttnChunk / kAttnWaves;
+constexpr int kAttnChunk = TT_ATTN_CHUNK;  // positions per chunk (a multiple of 32)
 constexpr int kAttnOob = 0x7FFFFF00;
 
 struct AttnArgs {
@@ -50,247 +40,232 @@ __device__ __forceinline__ uint4 attn_load16(__amdgpu_buffer_rsrc_t r, int off) 
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-__device__ __forceinline__ void attn_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+
+// Chunk pass, one wave per (16 NB positions, kv head).  Scores: S = K Q^T
+// on v_mfma_f32_16x16x32_bf16 per block of 16 positions, A = the key rows
+// (lane l: position l % 16, d = 32 kk + 8 (l / 16) .. +7: one 16-byte load),
+// B = the G query heads of the kv head as columns (heads past G are zero
+// columns); lane (head c, group q) gets positions 4q .. 4q+3 of the block.
+// The wave's maximum per head and p = exp2(s - max) stay in that layout,
+// which is the A layout of the next product: P V on the same instruction
+// with 32 positions per step (block 2m in elements 0..3, block 2m+1 in
+// 4..7), P split into bf16 hi + lo parts (p - hi is exact in fp32 and its
+// bf16 rounding leaves a 2^-18 relative residue) and V as B.  V goes to LDS
+// by buffer->LDS DMA in its row-major layout with the 16-byte chunks of row
+// r xor-swizzled, and comes back as B operands through ds_read_b64_tr_b16:
+// within each group of 16 lanes, source lane 4j + a addresses row j,
+// columns 4a .. 4a+3 of a 4 x 16 tile, and lane i receives column i, rows
+// 0..3.  No barrier across waves and no cross-lane reduction of P V.
+template <int D>
+__device__ __forceinline__ int attn_swz(int r) {
+    return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
 }
 
-// Sum / max over the LPT lanes of one position (16 or 8 consecutive lanes)
-// with DPP butterflies: quad swaps, then the half-row and row mirrors.
-template <int LPT>
-__device__ __forceinline__ float row_sum(float v) {
-    static_assert(LPT == 8 || LPT == 16, "lanes per position");
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                               0xB1, 0xF, 0xF, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                               0x4E, 0xF, 0xF, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                               0x141, 0xF, 0xF, false));
-    if (LPT == 16)
-        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                           0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
-    return v;
-}
-
-template <int D, int G>
-__global__ __launch_bounds__(64 * kAttnWaves) void k_attn_partial(AttnArgs a) {
-    constexpr int LPT = D / 8;                 // lanes per position
-    constexpr int PPL = 64 / LPT;              // positions per wave load
-    constexpr int NL = kAttnPerWave / PPL;     // loads per wave for K (and V)
-    constexpr int NR = kAttnWaves * PPL;       // position rows per workgroup
-    __shared__ float s_max[NR][G];
-    __shared__ float s_sum[NR][G];
-    __shared__ float s_o[NR][G][D];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+template <int D, int G, int NB>
+__global__ __launch_bounds__(64) void k_attn_partial(AttnArgs a) {
+    static_assert(NB % 2 == 0, "blocks of 16 positions come in pairs");
+    constexpr int KK = D / 32;           // score steps over d
+    constexpr int CPR = D / 8;           // 16-byte chunks per V row
+    constexpr int NV = 16 * NB * CPR / 64;  // V DMA instructions
+    constexpr int NT = D / 16;           // output column tiles
+    __shared__ __attribute__((aligned(16))) uint16_t s_v[16 * NB * D];
+    const int lane = threadIdx.x;
     const int c = blockIdx.x, g = blockIdx.y;
-    const int sl = lane % LPT, pg = lane / LPT;  // d-slice, position within a load
-    const int t0 = c * kAttnChunk + wave * kAttnPerWave;
+    const int t0 = c * 16 * NB;
+    const int col = lane & 15, grp = lane >> 4;
 
-    // 1. query slices of the G heads, then the key and value rows
     const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(a.q + (int64_t)g * G * D), 0, G * D * 2, 0x00020000);
-    uint4 qv[G];
-#pragma unroll
-    for (int i = 0; i < G; ++i) qv[i] = attn_load16(qr, (i * D + sl * 8) * 2);
     const int64_t head_off = (int64_t)g * a.tcap * D;
     const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(a.k + head_off), 0, a.T * D * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(a.v + head_off), 0, a.T * D * 2, 0x00020000);
-    uint4 kv[NL], vv[NL];
+
+    // 1. query columns, key rows, then V into LDS (rows past T read zeros)
+    uint4 qb[KK];
 #pragma unroll
-    for (int j = 0; j < NL; ++j) {
-        const int t = t0 + j * PPL + pg;
-        kv[j] = attn_load16(kr, t < a.T ? (t * D + sl * 8) * 2 : kAttnOob);
+    for (int kk = 0; kk < KK; ++kk)
+        qb[kk] = attn_load16(qr, col < G ? (col * D + 32 * kk + 8 * grp) * 2 : kAttnOob);
+    uint4 ka[NB][KK];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int t = t0 + 16 * b + col;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            ka[b][kk] = attn_load16(kr, t < a.T ? (t * D + 32 * kk + 8 * grp) * 2 : kAttnOob);
     }
 #pragma unroll
-    for (int j = 0; j < NL; ++j) {
-        const int t = t0 + j * PPL + pg;
-        vv[j] = attn_load16(vr, t < a.T ? (t * D + sl * 8) * 2 : kAttnOob);
+    for (int u = 0; u < NV; ++u) {
+        const int L = u * 64 + lane, r = L / CPR, x = (L % CPR) ^ attn_swz<D>(r);
+        const int t = t0 + r;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            vr, (__attribute__((address_space(3))) void *)(s_v + u * 512), 16,
+            t < a.T ? (t * D + 8 * x) * 2 : kAttnOob, 0, 0, 0);
     }
 
-    // 2. scores: dot2 over the lane's 8 elements, summed over the LPT lanes
-    //    of the position (xor-shuffles stay inside the position's lanes)
-    float s[NL][G];
+    // 2. scores in base-2 units, -inf past T; the wave's maximum per head
+    f32x4_t sc[NB];
 #pragma unroll
-    for (int j = 0; j < NL; ++j) {
+    for (int b = 0; b < NB; ++b) {
+        sc[b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int i = 0; i < G; ++i) {
-            float acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kv[j].x), as_bf16x2(qv[i].x),
-                                                        0.0f, false);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kv[j].y), as_bf16x2(qv[i].y), acc,
-                                                  false);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kv[j].z), as_bf16x2(qv[i].z), acc,
-                                                  false);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kv[j].w), as_bf16x2(qv[i].w), acc,
-                                                  false);
-            acc = row_sum<LPT>(acc);
-            const int t = t0 + j * PPL + pg;
-            s[j][i] = t < a.T ? acc * a.scale2 : -INFINITY;
+        for (int kk = 0; kk < KK; ++kk)
+            sc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, ka[b][kk]), __builtin_bit_cast(bf16x8_t, qb[kk]),
+                sc[b], 0, 0, 0);
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = t0 + 16 * b + 4 * grp + r;
+            sc[b][r] = t < a.T ? sc[b][r] * a.scale2 : -INFINITY;
+            m = fmaxf(m, sc[b][r]);
+        }
+    {
+        const uint32_t b16 = __builtin_bit_cast(uint32_t, m);
+        const f32x2_t r16 = __builtin_bit_cast(
+            f32x2_t, __builtin_amdgcn_permlane16_swap(b16, b16, false, false));
+        m = fmaxf(r16.x, r16.y);
+        const uint32_t b32 = __builtin_bit_cast(uint32_t, m);
+        const f32x2_t r32 = __builtin_bit_cast(
+            f32x2_t, __builtin_amdgcn_permlane32_swap(b32, b32, false, false));
+        m = fmaxf(r32.x, r32.y);
+    }
+
+    // 3. p = exp2(s - max) (0 past T), its sum, and the hi / lo A operands
+    //    (the chunk starts below T, so the maximum is finite)
+    float l = 0.0f;
+    bf16x8_t ph[NB / 2], pl[NB / 2];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float p = __builtin_amdgcn_exp2f(sc[b][r] - m);
+            l += p;
+            const __bf16 hi = (__bf16)p;
+            ph[b / 2][(b & 1) * 4 + r] = hi;
+            pl[b / 2][(b & 1) * 4 + r] = (__bf16)(p - (float)hi);
+        }
+    l = sum_xor32(sum_xor16(l));
+
+    // 4. O = P V per 16-column tile, V through transposing LDS reads
+    //    (source lane 4j + a of group q: row 4q + j of the block, columns
+    //    4a .. 4a+3 of the tile)
+    const int vj = (lane >> 2) & 3, va = lane & 3;
+    f32x4_t o[NT];
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) {
+        o[dt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        const int X = 2 * dt + (va >> 1);
+#pragma unroll
+        for (int mm = 0; mm < NB / 2; ++mm) {
+            i16x4_t h[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int r = 32 * mm + 16 * e + 4 * grp + vj;
+                const int off = (r * CPR + (X ^ attn_swz<D>(r))) * 16 + (va & 1) * 8;
+                h[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t *)(
+                        (__attribute__((address_space(3))) char *)s_v + off));
+            }
+            const bf16x8_t vb = __builtin_bit_cast(
+                bf16x8_t, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[mm], vb, o[dt], 0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[mm], vb, o[dt], 0, 0, 0);
         }
     }
 
-    // 3. the chunk's maximum per head: over the row's positions in
-    //    registers, then over the rows of all waves through LDS
-    const int row = wave * PPL + pg;
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-        float m = s[0][i];
-#pragma unroll
-        for (int j = 1; j < NL; ++j) m = fmaxf(m, s[j][i]);
-        if (sl == 0) s_max[row][i] = m;
-    }
-    attn_barrier();
-    float mx[G];
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-        mx[i] = s_max[0][i];
-#pragma unroll
-        for (int r = 1; r < NR; ++r) mx[i] = fmaxf(mx[i], s_max[r][i]);
-    }
-
-    // 4. p = exp(s - max), its sum and p * V in fp32
-    float o[G][8], l[G];
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-        l[i] = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[i][e] = 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < NL; ++j) {
-        const uint32_t vw[4] = {vv[j].x, vv[j].y, vv[j].z, vv[j].w};
-        float vf[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            vf[2 * e] = bf16_bits_to_f32(vw[e] & 0xFFFFu);
-            vf[2 * e + 1] = bf16_bits_to_f32(vw[e] >> 16);
-        }
-#pragma unroll
-        for (int i = 0; i < G; ++i) {
-            const float p = __builtin_amdgcn_exp2f(s[j][i] - mx[i]);  // 0 past T
-            l[i] += p;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[i][e] = fmaf(p, vf[e], o[i][e]);
-        }
-    }
-    // each row's partial sums go to LDS (a row's lanes hold its d-slices)
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-        float4 *dst = reinterpret_cast<float4 *>(&s_o[row][i][sl * 8]);
-        dst[0] = make_float4(o[i][0], o[i][1], o[i][2], o[i][3]);
-        dst[1] = make_float4(o[i][4], o[i][5], o[i][6], o[i][7]);
-        if (sl == 0) s_sum[row][i] = l[i];
-    }
-    attn_barrier();
-
-    // 5. fixed-order sum over the rows, to the workspace
+    // 5. the chunk's partial sums: lane (column c, group q) holds heads
+    //    4q .. 4q+3 of columns dt * 16 + c
     const int64_t slot = (int64_t)g * a.nchunks + c;
-    for (int idx = tid; idx < G * D; idx += blockDim.x) {
-        const int i = idx / D, e = idx - i * D;
-        float v = s_o[0][i][e];
 #pragma unroll
-        for (int r = 1; r < NR; ++r) v += s_o[r][i][e];
-        a.part[slot * G * D + idx] = v;
-    }
-    if (tid < G) {
-        float v = s_sum[0][tid], m = s_max[0][tid];
+    for (int dt = 0; dt < NT; ++dt)
 #pragma unroll
-        for (int r = 1; r < NR; ++r) {
-            v += s_sum[r][tid];
-            m = fmaxf(m, s_max[r][tid]);
+        for (int r = 0; r < 4; ++r) {
+            const int head = 4 * grp + r;
+            if (head < G) a.part[(slot * G + head) * D + dt * 16 + col] = o[dt][r];
         }
-        a.ml[(slot * G + tid) * 2] = m;
-        a.ml[(slot * G + tid) * 2 + 1] = v;
+    if (lane < G) {
+        a.ml[(slot * G + lane) * 2] = m;
+        a.ml[(slot * G + lane) * 2 + 1] = l;
     }
 }
 
-// One workgroup of 256 threads per query head h = g * G + i.  The chunks go
-// in rounds of 64: every thread issues its loads for the round at once
-// (thread (e, part) takes element e of chunks part, part + S, ...; wave 0
-// takes the chunks' (max, sum)), then wave 0 forms the round maximum, the
-// factors exp(m_c - M) and the round's sum, and every thread rescales its
-// running sum -- one memory round trip per round.  The parts are added in a
-// fixed order at the end.
-constexpr int kCombThreads = 256;
-constexpr int kCombRound = 64;
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-    return v;
+// Wave-wide maximum / sum: DPP butterflies inside each row of 16 lanes (quad
+// swaps, half-row and row mirrors), then the two row swaps.  Every lane ends
+// with the same bits.  All 64 lanes must be active.
+template <bool MAX>
+__device__ __forceinline__ float wave_reduce(float v) {
+    auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+    v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                            0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+    v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                            0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+    v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                            0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
+    v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                            0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
+    const uint32_t b16 = __builtin_bit_cast(uint32_t, v);
+    const f32x2_t r16 =
+        __builtin_bit_cast(f32x2_t, __builtin_amdgcn_permlane16_swap(b16, b16, false, false));
+    v = op(r16.x, r16.y);
+    const uint32_t b32 = __builtin_bit_cast(uint32_t, v);
+    const f32x2_t r32 =
+        __builtin_bit_cast(f32x2_t, __builtin_amdgcn_permlane32_swap(b32, b32, false, false));
+    return op(r32.x, r32.y);
 }
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce<true>(v); }
+__device__ __forceinline__ float wave_sum(float v) { return wave_reduce<false>(v); }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    return v;
-}
-
+// One wave per (query head h = g * G + i, 64 output columns): lane k takes
+// chunk c0 + k's (max, sum) and the wave maximum gives every chunk's factor
+// exp2(m_c - M); lane e accumulates column e over the chunks of the round
+// with each factor read from its chunk's lane (v_readlane), in four
+// interleaved partial sums added in a fixed order.  Rounds of 64 chunks
+// rescale the running sums to the new maximum.  No LDS and no barrier.
 template <int D, int G>
-__global__ __launch_bounds__(kCombThreads) void k_attn_combine(AttnArgs a) {
-    constexpr int S = kCombThreads / D;     // chunk parts per element
-    constexpr int PER = kCombRound / S;     // chunks per thread per round
-    __shared__ float fac[kCombRound];
-    __shared__ float stat[2];               // round maximum, round sum
-    __shared__ float opart[S][D];
-    const int h = blockIdx.x, tid = threadIdx.x;
+__global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
+    const int h = blockIdx.x, lane = threadIdx.x;
     const int g = h / G, i = h - g * G;
+    const int e = blockIdx.y * 64 + lane;
     const int nc = a.nchunks;
-    const int e = tid % D, p = tid / D;
-    // chunk c of this head: part at ((g * nc + c) * G + i) * D, (max, sum) at
-    // ((g * nc + c) * G + i) * 2
     const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
         a.part + (int64_t)g * nc * G * D, 0, nc * G * D * 4, 0x00020000);
     const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(
         a.ml + (int64_t)g * nc * G * 2, 0, nc * G * 2 * 4, 0x00020000);
     float M = -INFINITY, L = 0.0f, o = 0.0f;
-    for (int c0 = 0; c0 < nc; c0 += kCombRound) {
-        float pv[PER];
+    for (int c0 = 0; c0 < nc; c0 += 64) {
+        const int n = min(64, nc - c0);
+        const f32x2_t ml = __builtin_bit_cast(
+            f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
+                         mr, lane < n ? ((c0 + lane) * G + i) * 8 : kAttnOob, 0, 0));
+        float pv[64];
 #pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            const int c = c0 + p + S * u;
+        for (int u = 0; u < 64; ++u)
             pv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                pr, c < nc ? ((c * G + i) * D + e) * 4 : kAttnOob, 0, 0));
-        }
-        float m = -INFINITY, l = 0.0f;
-        if (tid < kCombRound && c0 + tid < nc) {
-            m = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                mr, ((c0 + tid) * G + i) * 8, 0, 0));
-            l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                mr, ((c0 + tid) * G + i) * 8 + 4, 0, 0));
-        }
-        if (tid < kCombRound) {
-            const float Mn = fmaxf(M, wave_max(m));
-            const float f = c0 + tid < nc ? __builtin_amdgcn_exp2f(m - Mn) : 0.0f;
-            fac[tid] = f;
-            const float ls = wave_sum(l * f);
-            if (tid == 0) {
-                stat[0] = Mn;
-                stat[1] = ls;
-            }
-        }
-        __syncthreads();
-        const float Mn = stat[0];
+                                                  pr, u < n ? ((c0 + u) * G + i) * D * 4 + e * 4
+                                                            : kAttnOob, 0, 0));
+        // every load of the round is issued before the first use of any
+        __builtin_amdgcn_sched_barrier(0);
+        const float m = lane < n ? ml.x : -INFINITY;
+        const float Mn = fmaxf(M, wave_max(m));
+        const float f = lane < n ? __builtin_amdgcn_exp2f(m - Mn) : 0.0f;
         const float r = __builtin_amdgcn_exp2f(M - Mn);  // 0 on the first round
-        float acc = 0.0f;
+        L = fmaf(L, r, wave_sum(lane < n ? ml.y * f : 0.0f));
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int u = 0; u < PER; ++u) acc = fmaf(pv[u], fac[p + S * u], acc);
-        o = fmaf(o, r, acc);
-        L = fmaf(L, r, stat[1]);
+        for (int u = 0; u < 64; ++u)
+            acc[u & 3] = fmaf(pv[u], __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                                  __builtin_bit_cast(int, f), u)),
+                              acc[u & 3]);
+        o = fmaf(o, r, (acc[0] + acc[1]) + (acc[2] + acc[3]));
         M = Mn;
-        __syncthreads();
     }
-    opart[p][e] = o;
-    __syncthreads();
-    if (p == 0) {
-        float v = opart[0][e];
-#pragma unroll
-        for (int q = 1; q < S; ++q) v += opart[q][e];
-        store_out(a.out, (int64_t)h * D + e, v / L, a.out_bf16);
-    }
+    store_out(a.out, (int64_t)h * D + e, o / L, a.out_bf16);
 }
 
 namespace {
@@ -299,10 +274,10 @@ int64_t attn_chunks(int64_t T) { return ceil_div(T, kAttnChunk); }
 
 template <int D, int G>
 tt_status launch_attn(const AttnArgs &a, hipStream_t s) {
-    TT_TRY(launch("gqa attention (chunks)", k_attn_partial<D, G>,
-                  dim3((unsigned)a.nchunks, (unsigned)a.hkv), dim3(64 * kAttnWaves), 0, s, a));
-    return launch("gqa attention (combine)", k_attn_combine<D, G>, dim3((unsigned)a.hq),
-                  dim3(kCombThreads), 0, s, a);
+    TT_TRY(launch("gqa attention (chunks)", k_attn_partial<D, G, kAttnChunk / 16>,
+                  dim3((unsigned)a.nchunks, (unsigned)a.hkv), dim3(64), 0, s, a));
+    return launch("gqa attention (combine)", k_attn_combine<D, G>,
+                  dim3((unsigned)a.hq, (unsigned)(D / 64)), dim3(64), 0, s, a);
 }
 
 template <int D>

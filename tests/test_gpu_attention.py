@@ -1,12 +1,14 @@
 """Single-token GQA attention on the device vs the CPU oracle, through the C
 ABI: Phi-4-shaped heads (40 / 10 x 128) and gpt-oss-shaped heads (64 / 8 x
-64) at short and long contexts, ragged T, bf16 output, a cache with spare
-capacity, T = 1, and run-to-run identity.
+64) at short and long contexts, every supported group size G = hq / hkv (1,
+2, 4, 8) at d = 64 and 128, ragged T, bf16 output, a cache with spare
+capacity, T = 1, scores spread over a wide range, and run-to-run identity.
 
-Tolerance: with score errors below 1e-5 * Smax (fp32 sums of 128 products
-are good to a few 1e-6 relative) the softmax weights move by at most a
-factor exp(±2e-5 Smax), so |out - ref| <= (2e-3 + 4e-5 * Smax) * A,
-A = sum_t p_t |V| per element, plus the spec cosine bound."""
+Tolerance: scores are bf16 x bf16 products (exact in fp32) accumulated in
+fp32 on the matrix cores, and the softmax weights enter P V as two bf16
+parts (residue 2^-18 relative).  With score errors below 1e-5 * Smax the
+weights move by at most a factor exp(+-2e-5 Smax), so |out - ref| <= (2e-3 +
+4e-5 * Smax) * A, A = sum_t p_t |V| per element, plus the cosine bound."""
 import numpy as np
 import pytest
 import torch
@@ -19,10 +21,13 @@ from _parity import assert_parity, dev_bf16, to_np
 pytestmark = pytest.mark.gpu
 
 
-def _case(dev, hq, hkv, d, tcap, T, seed, out_dtype=torch.float32):
+def _case(dev, hq, hkv, d, tcap, T, seed, out_dtype=torch.float32, q_mul=1.0, k_spread=0):
     gen = np.random.default_rng(seed)
-    q = workloads.bf16_bits(gen.standard_normal((hq, d)).astype(np.float32))
-    K = workloads.bf16_bits(gen.standard_normal((hkv, tcap, d)).astype(np.float32))
+    q = workloads.bf16_bits((q_mul * gen.standard_normal((hq, d))).astype(np.float32))
+    kf = gen.standard_normal((hkv, tcap, d))
+    if k_spread:
+        kf = kf * np.exp2(gen.integers(-k_spread, k_spread + 1, kf.shape))
+    K = workloads.bf16_bits(kf.astype(np.float32))
     V = workloads.bf16_bits(gen.standard_normal((hkv, tcap, d)).astype(np.float32))
     scale = 1.0 / np.sqrt(d)
     out = tt.gqa_attention_decode(dev_bf16(q, dev), dev_bf16(K, dev), dev_bf16(V, dev), hq, hkv,
@@ -37,10 +42,20 @@ def _case(dev, hq, hkv, d, tcap, T, seed, out_dtype=torch.float32):
 
 @pytest.mark.parametrize("hq,hkv,d,T", [(40, 10, 128, 1), (40, 10, 128, 63), (40, 10, 128, 256),
                                         (40, 10, 128, 4096), (64, 8, 64, 100),
-                                        (64, 8, 64, 2049), (8, 8, 128, 300), (4, 2, 64, 65)])
+                                        (64, 8, 64, 2049), (8, 8, 128, 300), (4, 2, 64, 65),
+                                        (32, 4, 128, 517), (16, 16, 64, 33), (16, 8, 128, 1),
+                                        (32, 8, 64, 4097), (8, 4, 64, 16), (16, 2, 128, 8192)])
 def test_gqa_attention(dev, hq, hkv, d, T):
     got, ref, tol = _case(dev, hq, hkv, d, T, T, hq * 7 + T)
     assert_parity(got, ref, tol, f"attention hq{hq} hkv{hkv} d{d} T{T}")
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(40, 10, 128), (64, 8, 64)])
+def test_gqa_attention_wide_range_scores(dev, hq, hkv, d):
+    # q x 6 and key elements scaled by 2^-6 .. 2^6: scores of magnitude ~50
+    # and products spread over 24 binades inside every dot product
+    got, ref, tol = _case(dev, hq, hkv, d, 700, 700, 31 + d, q_mul=6.0, k_spread=6)
+    assert_parity(got, ref, tol, f"attention wide-range scores hq{hq} d{d}")
 
 
 def test_gqa_attention_spare_capacity_and_bf16_out(dev):
