@@ -13,11 +13,11 @@
 // 16-row tiles would leave half the chip idle.
 //
 // One workgroup per tile and NT tokens; wave p owns units [p UPW, p UPW +
-// UPW).  Issue order per wave: its share of the activations (straight-line
+// UPW).  Issue order per wave: the activations its units read (straight-line
 // buffer loads, zeros past k and past the batch), then its UPW code units,
-// then -- in wave 0 -- the tile's row scales.  The activations go to LDS as
-// they are; after an LDS-only barrier each unit is consumed as its load
-// lands.  fp32 activations: v_cvt_scalef32_pk_f32_fp8 (scale 1) turns two
+// then -- in wave 0 -- the tile's row scales.  The activations go to the
+// wave's own part of LDS as they are (no barrier: no other wave reads them);
+// each unit is consumed as its load lands.  fp32 activations: v_cvt_scalef32_pk_f32_fp8 (scale 1) turns two
 // E4M3 codes into two exact fp32 values, one FMA per element accumulates.
 // bf16 activations: v_cvt_scalef32_pk_bf16_fp8 turns two codes into two exact
 // bf16 values and one dot2 takes the pair (4 instead of 6 VALU ops per 4
@@ -83,23 +83,23 @@ __global__ __launch_bounds__(1024) void k_fp8_gemv(F8Args a) {
     float *xs = reinterpret_cast<float *>(smem);  // [NT][kp] fp32, or bf16 as uint16
     float *red = reinterpret_cast<float *>(smem + (size_t)NT * kp * XSZ);  // [ks][NT][8]
     const int tid = threadIdx.x, lane = tid & 63;
-    const int nthreads = blockDim.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tile = blockIdx.x, t0 = blockIdx.y * NT;
     const int nt = min(NT, a.batch - t0);
 
-    // 1. activations: 16-byte chunks of 4 fp32 or 8 bf16 elements; per
-    //    token a thread takes UPW / 2 (fp32) or UPW / 4 (bf16) chunks
+    // 1. activations of the wave's own units: 16-byte chunks of 4 fp32 or 8
+    //    bf16 elements, chunk j * 64 + lane of the wave's slice per token
     constexpr int EPC = XF32 ? 4 : 8;
-    constexpr int XC = NT * (XF32 ? UPW / 2 : UPW / 4);
-    const int chunks = kp / EPC;  // per token
+    constexpr int XL = XF32 ? UPW / 2 : UPW / 4;  // chunks per lane per token
+    constexpr int XC = NT * XL;
+    const int u0 = wave * UPW;
+    const int cw0 = u0 * kF8UnitK / EPC;  // first chunk of the wave's slice
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void *>(a.x), 0, a.batch * a.k * (XF32 ? 4 : 2), 0x00020000);
     uint4 xv[XC];
 #pragma unroll
     for (int c = 0; c < XC; ++c) {
-        const int idx = tid + c * nthreads;
-        const int t = idx / chunks, e0 = (idx - t * chunks) * EPC;
+        const int t = c / XL, e0 = (cw0 + (c % XL) * 64 + lane) * EPC;
         const bool ok = t < nt && e0 < a.k;
         xv[c] = f8_load16(xr, ok ? ((t0 + t) * a.k + e0) * (XF32 ? 4 : 2) : kF8Oob);
     }
@@ -109,7 +109,6 @@ __global__ __launch_bounds__(1024) void k_fp8_gemv(F8Args a) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t *>(a.w + (int64_t)tile * a.tile_stride), 0, (int)a.tile_stride,
         0x00020000);
-    const int u0 = wave * UPW;
     uint4 cu[UPW];
 #pragma unroll
     for (int i = 0; i < UPW; ++i)
@@ -118,14 +117,16 @@ __global__ __launch_bounds__(1024) void k_fp8_gemv(F8Args a) {
         float, __builtin_amdgcn_raw_buffer_load_b32(
                    rs, (wave == 0 && lane < kF8TileRows) ? a.scale_off + lane * 4 : kF8Oob, 0, 0));
 
-    // 3. activations to LDS as they are (fp32 or bf16), then an LDS-only
-    //    barrier
+    // 3. the slice to LDS as it is (fp32 or bf16); only this wave reads it
+    //    back, and a wave's LDS accesses complete in order: no barrier
 #pragma unroll
     for (int c = 0; c < XC; ++c) {
-        const int idx = tid + c * nthreads;
-        if (idx < NT * chunks) reinterpret_cast<uint4 *>(xs)[idx] = xv[c];
+        const int t = c / XL;
+        reinterpret_cast<uint4 *>(xs)[t * (kp / EPC) + cw0 + (c % XL) * 64 + lane] = xv[c];
     }
-    f8_lds_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 
     // 4. consume the units in load order: lane (r, q) covers k = 128 u + 16 q
     const int q = lane >> 3;

@@ -92,36 +92,38 @@ __global__ __launch_bounds__(1024) void k_int4_gemv(I4Args a) {
     const int tile = blockIdx.x, t0 = blockIdx.y * NT;
     const int nt = min(NT, a.batch - t0);
 
-    // 1. activations: thread tid fetches piece tid of every token.  Rows of
-    //    16-byte aligned x go out as straight-line buffer loads (zeros past
-    //    the batch and past k), so the weight loads follow without a wait;
-    //    other rows take element loads.
-    uint32_t xw[NT][16];
+    // 1. activations: each wave fetches the slice of every token that its
+    //    own units read (UPW * 128 elements, one 8-element group per lane
+    //    per load), so no other wave waits on it.  Rows of 16-byte aligned x
+    //    go out as straight-line buffer loads (zeros past the batch and past
+    //    k); other rows take element loads.
+    constexpr int XL = UPW / 4;  // loads per lane per token
+    const int kw = wave * UPW * 128;  // first element of the wave's slice
+    uint32_t xw[NT][XL][4];
     {
-        const int p = tid;
         const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t *>(a.x), 0, XVEC ? a.batch * a.k * 2 : 0, 0x00020000);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const uint16_t *src = a.x + (int64_t)(t0 + t) * a.k + p * 32;
             const bool tok_ok = t < nt;
-            if (XVEC) {
 #pragma unroll
-                for (int g8 = 0; g8 < 4; ++g8) {
-                    const bool ok = tok_ok && p * 32 + g8 * 8 < a.k;
-                    const uint4 v = i4_load16(xr, ok ? ((t0 + t) * a.k + p * 32 + g8 * 8) * 2 : kOob);
-                    xw[t][4 * g8 + 0] = v.x;
-                    xw[t][4 * g8 + 1] = v.y;
-                    xw[t][4 * g8 + 2] = v.z;
-                    xw[t][4 * g8 + 3] = v.w;
-                }
-            } else {
+            for (int j = 0; j < XL; ++j) {
+                const int k0 = kw + (j * 64 + lane) * 8;
+                if (XVEC) {
+                    const bool ok = tok_ok && k0 < a.k;
+                    const uint4 v = i4_load16(xr, ok ? ((t0 + t) * a.k + k0) * 2 : kOob);
+                    xw[t][j][0] = v.x;
+                    xw[t][j][1] = v.y;
+                    xw[t][j][2] = v.z;
+                    xw[t][j][3] = v.w;
+                } else {
+                    const uint16_t *src = a.x + (int64_t)(t0 + t) * a.k + k0;
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int k0 = p * 32 + 2 * j;
-                    const uint32_t lo = (tok_ok && k0 < a.k) ? src[2 * j] : 0u;
-                    const uint32_t hi = (tok_ok && k0 + 1 < a.k) ? src[2 * j + 1] : 0u;
-                    xw[t][j] = lo | (hi << 16);
+                    for (int d = 0; d < 4; ++d) {
+                        const uint32_t lo = (tok_ok && k0 + 2 * d < a.k) ? src[2 * d] : 0u;
+                        const uint32_t hi = (tok_ok && k0 + 2 * d + 1 < a.k) ? src[2 * d + 1] : 0u;
+                        xw[t][j][d] = lo | (hi << 16);
+                    }
                 }
             }
         }
@@ -150,29 +152,36 @@ __global__ __launch_bounds__(1024) void k_int4_gemv(I4Args a) {
             c[i] = i4_load16(rs, i < n ? voff + i * kUnitBytes : kOob);
     }
 
-    // 3. activations to LDS: 8-element groups reordered as (x0,x4) (x1,x5)
-    //    (x2,x6) (x3,x7), plus the plain sum of each 32-element piece
-    if (tid < pieces) {
+    // 3. the wave's slice to LDS: 8-element groups reordered as (x0,x4)
+    //    (x1,x5) (x2,x6) (x3,x7), and the plain sum of each 32-element piece
+    //    (the four lanes of a piece add theirs with two DPP quad swaps).  Only
+    //    this wave reads the slice back, and a wave's LDS accesses complete in
+    //    order, so no barrier is needed.
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            uint4 *dst = reinterpret_cast<uint4 *>(xs + t * kp + tid * 32);
-            float sum = 0.0f;
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int g8 = 0; g8 < 4; ++g8) {
-                const uint32_t w0 = xw[t][4 * g8], w1 = xw[t][4 * g8 + 1];
-                const uint32_t w2 = xw[t][4 * g8 + 2], w3 = xw[t][4 * g8 + 3];
-                // elements e0..e7 = lo(w0) hi(w0) lo(w1) hi(w1) lo(w2) hi(w2) lo(w3) hi(w3)
-                dst[g8] = make_uint4((w0 & 0xFFFFu) | (w2 << 16), (w0 >> 16) | (w2 & 0xFFFF0000u),
-                                     (w1 & 0xFFFFu) | (w3 << 16), (w1 >> 16) | (w3 & 0xFFFF0000u));
-                sum += bf16_bits_to_f32(w0 & 0xFFFFu) + bf16_bits_to_f32(w0 >> 16) +
-                       bf16_bits_to_f32(w1 & 0xFFFFu) + bf16_bits_to_f32(w1 >> 16) +
-                       bf16_bits_to_f32(w2 & 0xFFFFu) + bf16_bits_to_f32(w2 >> 16) +
-                       bf16_bits_to_f32(w3 & 0xFFFFu) + bf16_bits_to_f32(w3 >> 16);
-            }
-            xsum[t * pieces + tid] = sum;
+        for (int j = 0; j < XL; ++j) {
+            const uint32_t w0 = xw[t][j][0], w1 = xw[t][j][1];
+            const uint32_t w2 = xw[t][j][2], w3 = xw[t][j][3];
+            // elements e0..e7 = lo(w0) hi(w0) lo(w1) hi(w1) lo(w2) hi(w2) lo(w3) hi(w3)
+            *reinterpret_cast<uint4 *>(xs + t * kp + kw + (j * 64 + lane) * 8) =
+                make_uint4((w0 & 0xFFFFu) | (w2 << 16), (w0 >> 16) | (w2 & 0xFFFF0000u),
+                           (w1 & 0xFFFFu) | (w3 << 16), (w1 >> 16) | (w3 & 0xFFFF0000u));
+            float sum = (bf16_bits_to_f32(w0 & 0xFFFFu) + bf16_bits_to_f32(w0 >> 16)) +
+                        (bf16_bits_to_f32(w1 & 0xFFFFu) + bf16_bits_to_f32(w1 >> 16)) +
+                        (bf16_bits_to_f32(w2 & 0xFFFFu) + bf16_bits_to_f32(w2 >> 16)) +
+                        (bf16_bits_to_f32(w3 & 0xFFFFu) + bf16_bits_to_f32(w3 >> 16));
+            sum += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                 0, __builtin_bit_cast(int, sum), 0xB1, 0xF, 0xF,
+                                                 false));
+            sum += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                 0, __builtin_bit_cast(int, sum), 0x4E, 0xF, 0xF,
+                                                 false));
+            if ((lane & 3) == 0) xsum[t * pieces + kw / 32 + j * 16 + (lane >> 2)] = sum;
         }
-    }
-    i4_lds_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 
     // 4. consume the units in load order
     float acc[NT];

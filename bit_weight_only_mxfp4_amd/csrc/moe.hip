@@ -108,6 +108,15 @@ struct DownArgs {
 #endif
 constexpr int kDownOob = 0x7FFFFF00;
 
+// Orders a wave's own LDS writes before its later LDS reads (the hardware
+// completes one wave's LDS accesses in order; this keeps the compiler from
+// moving them across).
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
 __device__ __forceinline__ void down_lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
@@ -133,7 +142,7 @@ __global__ __launch_bounds__(1024) void k_down_combine(DownArgs a) {
     uint4 *xs4 = reinterpret_cast<uint4 *>(smem);
     float *red = reinterpret_cast<float *>(smem + (size_t)spr * kp * ESZ);  // [topk][S][16]
     float *pss = red + topk * S * 16;                                       // [topk][17]
-    const int tid = threadIdx.x, lane = tid & 63, nthreads = blockDim.x;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tile = blockIdx.x, b = blockIdx.y;
     const int q = lane >> 4;
@@ -148,14 +157,15 @@ __global__ __launch_bounds__(1024) void k_down_combine(DownArgs a) {
         const int e = slot_ok ? a.ids[b * topk + j] : -1;
         const bool valid = e >= 0 && e < a.n_experts;
 
-        // 1. activations of slots jb .. jb + spr - 1
+        // 1. the activations this wave's units read: slot j, chunks
+        //    part * UPW * 32 + c * 64 + lane (4 fp32 each)
+        const int cw0 = part * UPW * 32;
         uint4 hv[XC];
 #pragma unroll
         for (int c = 0; c < XC; ++c) {
-            const int idx = tid + c * nthreads;
-            const int jj = jb + idx / slot_chunks, off = idx % slot_chunks;
-            hv[c] = (jj < topk && off < valid_chunks) ? hsrc[jj * valid_chunks + off]
-                                                     : make_uint4(0, 0, 0, 0);
+            const int ci = cw0 + c * 64 + lane;
+            hv[c] = (slot_ok && ci < valid_chunks) ? hsrc[j * valid_chunks + ci]
+                                                  : make_uint4(0, 0, 0, 0);
         }
 
         // 2. weights
@@ -186,14 +196,12 @@ __global__ __launch_bounds__(1024) void k_down_combine(DownArgs a) {
                        rs, (part == 0 && lane < 16) ? a.ps_off + lane * 4 : kDownOob, 0, 0));
         const float wj = slot_ok ? a.wt[b * topk + j] : 0.0f;
 
-        // 3. activations to LDS (after the previous round finished reading)
-        if (jb > 0) down_lds_barrier();
+        // 3. activations to the wave's own part of LDS (only this wave reads
+        //    it, in this round and the next: a wave's LDS accesses complete
+        //    in order, so no barrier)
 #pragma unroll
-        for (int cc = 0; cc < XC; ++cc) {
-            const int idx = tid + cc * nthreads;
-            if (idx < spr * slot_chunks) xs4[idx] = hv[cc];
-        }
-        down_lds_barrier();
+        for (int cc = 0; cc < XC; ++cc) xs4[js * slot_chunks + cw0 + cc * 64 + lane] = hv[cc];
+        wave_lds_fence();
 
         // 4. consume the units in load order
         float acc = 0.0f;
@@ -238,11 +246,11 @@ __global__ __launch_bounds__(1024) void k_down_mx(DownArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int S = a.S, topk = a.topk, spr = a.spr;
     const int kp = S * UPW * 128;                // staged K per slot, zero past inter
-    const int kpc = kp / 8, kpu = kp / 128;
+    const int kpu = kp / 128;
     const int qsz = spr * 2 * kp, zoff = qsz + spr * kp / 16;
     float *red = reinterpret_cast<float *>(smem + zoff + 32);  // [topk][S][16]
     float *pss = red + topk * S * 16;                          // [topk][17]
-    const int tid = threadIdx.x, lane = tid & 63, nthreads = blockDim.x;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tile = blockIdx.x, b = blockIdx.y;
     const int js = wave / S, part = wave - js * S;
@@ -258,14 +266,15 @@ __global__ __launch_bounds__(1024) void k_down_mx(DownArgs a) {
         const int e = slot_ok ? a.ids[b * topk + j] : -1;
         const bool valid = e >= 0 && e < a.n_experts;
 
-        // 1. activations of slots jb .. jb + spr - 1 (XC * nthreads = spr * kpc)
+        // 1. the activations this wave's units read: slot j, chunks
+        //    part * UPW * 16 + c * 64 + lane (8 bf16 each)
+        const int cw0 = part * UPW * 16;
         uint4 hv[XC];
 #pragma unroll
         for (int c = 0; c < XC; ++c) {
-            const int idx = tid + c * nthreads;
-            const int jj = jb + idx / kpc, off = idx % kpc;
-            hv[c] = (jj < topk && off < valid_chunks) ? hsrc[jj * valid_chunks + off]
-                                                     : make_uint4(0, 0, 0, 0);
+            const int ci = cw0 + c * 64 + lane;
+            hv[c] = (slot_ok && ci < valid_chunks) ? hsrc[j * valid_chunks + ci]
+                                                  : make_uint4(0, 0, 0, 0);
         }
 
         // 2. weights
@@ -297,25 +306,25 @@ __global__ __launch_bounds__(1024) void k_down_mx(DownArgs a) {
         const float wj = slot_ok ? a.wt[b * topk + j] : 0.0f;
         __builtin_amdgcn_sched_barrier(0);
 
-        // 3. activations -> E4M3 parts in LDS (after the previous round
-        //    finished reading)
-        if (jb > 0) down_lds_barrier();
+        // 3. activations -> E4M3 parts in the wave's own part of LDS (only
+        //    this wave reads it, in this round and the next; every wave
+        //    writes the same zeros to the shared zero slot before it reads
+        //    it; a wave's LDS accesses complete in order, so no barrier)
 #pragma unroll
         for (int cc = 0; cc < XC; ++cc) {
-            const int idx = tid + cc * nthreads;
-            const int jl = idx / kpc, ci = idx % kpc;
+            const int ci = cw0 + cc * 64 + lane;
             uint2 hi, lo;
             const uint32_t sh = split_chunk(hv[cc], &hi, &lo);
-            *reinterpret_cast<uint2 *>(smem + (jl * 2) * kp + ci * 8) = hi;
-            *reinterpret_cast<uint2 *>(smem + (jl * 2 + 1) * kp + ci * 8) = lo;
+            *reinterpret_cast<uint2 *>(smem + (js * 2) * kp + ci * 8) = hi;
+            *reinterpret_cast<uint2 *>(smem + (js * 2 + 1) * kp + ci * 8) = lo;
             if ((ci & 3) == 0) {
                 const int blk = ci >> 2;
-                smem[qsz + ((jl * 2) * 4 + (blk & 3)) * kpu + (blk >> 2)] = (uint8_t)sh;
-                smem[qsz + ((jl * 2 + 1) * 4 + (blk & 3)) * kpu + (blk >> 2)] = (uint8_t)(sh - 4u);
+                smem[qsz + ((js * 2) * 4 + (blk & 3)) * kpu + (blk >> 2)] = (uint8_t)sh;
+                smem[qsz + ((js * 2 + 1) * 4 + (blk & 3)) * kpu + (blk >> 2)] = (uint8_t)(sh - 4u);
             }
         }
-        if (tid < 8) reinterpret_cast<uint32_t *>(smem + zoff)[tid] = 0u;
-        down_lds_barrier();
+        if (lane < 8) reinterpret_cast<uint32_t *>(smem + zoff)[lane] = 0u;
+        wave_lds_fence();
 
         // 4. the units in load order, one scaled MFMA each
         const int qbase = bact ? (js * 2 + hl) * kp + u0 * 128 + 16 * grp : zoff;
