@@ -270,14 +270,16 @@ __global__ __launch_bounds__(1024) void k_gateup_mx(GateUpArgs a) {
         for (int i = 4 * g; i < 4 * g + 4; ++i)
             c[i] = load16(rs, i < n ? voff + i * kUnitBytes : kOob);
     }
-    // postscales of gate row r and up row r + 8 for the finishing lanes
-    // (lane 8t + r, r < 8), fetched with the weights
+    // postscales for the finishing lanes (lane 8t + r finishes gate row r
+    // and up row r + 8), fetched with the weights by the finishing wave
+    // only: lane l loads row l % 16, and a DPP rotate by 8 inside the row of
+    // 16 lanes brings the partner row
     const int fr = lane & 7;
     const bool fin = part == 0 && tile_ok;
-    const float psg = __builtin_bit_cast(
-        float, __builtin_amdgcn_raw_buffer_load_b32(rs, fin ? a.ps_off + fr * 4 : kOob, 0, 0));
-    const float psu = __builtin_bit_cast(
-        float, __builtin_amdgcn_raw_buffer_load_b32(rs, fin ? a.ps_off + (fr + 8) * 4 : kOob, 0, 0));
+    float ps_own = 0.0f;
+    if (fin)  // uniform
+        ps_own = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rs, a.ps_off + (lane & 15) * 4, 0, 0));
     // keep every load above the activation split
     __builtin_amdgcn_sched_barrier(0);
 
@@ -335,7 +337,13 @@ __global__ __launch_bounds__(1024) void k_gateup_mx(GateUpArgs a) {
         *reinterpret_cast<f32x4_t *>(red + (wave * NTOK + col) * 16 + 4 * grp) = y;
     lds_barrier();
     const int ft = lane >> 3;
-    if (part != 0 || !tile_ok || ft >= ntok) return;
+    if (part != 0 || !tile_ok) return;
+    const float ps_other = __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, ps_own), 0x128, 0xF, 0xF,
+                                           false));
+    const float psg = (lane & 8) ? ps_other : ps_own;
+    const float psu = (lane & 8) ? ps_own : ps_other;
+    if (ft >= ntok) return;
     float g = 0.0f, u = 0.0f;
     for (int p = 0; p < ks; ++p) {
         const float *rp = red + ((tsub * ks + p) * NTOK + ft) * 16;
