@@ -52,7 +52,8 @@ def _case(dev, n, k, batch, xf32, rows=None, out_dtype=torch.float32, seed=0):
 @pytest.mark.parametrize("n,k,batch,xf32", [(13, 200, 1, True), (8, 128, 1, False),
                                             (100, 1000, 3, False), (40, 4096, 8, True),
                                             (17, 2880, 32, False), (333, 11008, 2, True),
-                                            (9, 32768, 1, True), (1, 8, 1, False)])
+                                            (9, 32768, 1, True), (9, 32768, 1, False),
+                                            (5, 16384, 4, False), (1, 8, 1, False)])
 def test_fp8_gemv_ragged(dev, n, k, batch, xf32):
     got, ref, S = _case(dev, n, k, batch, xf32)
     assert_parity(got, ref, gemv_tol(S, ref), f"fp8 n{n} k{k} b{batch} {'f32' if xf32 else 'bf16'}")

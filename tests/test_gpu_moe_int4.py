@@ -200,7 +200,8 @@ def _int4_case(dev, n, k, batch, layer=0, tensor=workloads.T_INT4W):
 
 
 @pytest.mark.parametrize("n,k,batch", [(7680, 5120, 1), (5120, 5120, 1), (100, 200, 1),
-                                       (48, 328, 3), (33, 5120, 8), (16, 2, 1), (40, 130, 32)])
+                                       (48, 328, 3), (33, 5120, 8), (16, 2, 1), (40, 130, 32),
+                                       (64, 16384, 1), (40, 16384, 3), (24, 1002, 2)])
 def test_int4_gemv(dev, n, k, batch):
     q, s, z, packed, x = _int4_case(dev, n, k, batch)
     y = tt.int4_gemv(packed, n, k, dev_bf16(x, dev))
@@ -213,6 +214,21 @@ def test_int4_gemv(dev, n, k, batch):
         got = got[:, rows]
     yr, S = oracle.int4_gemv(q, s, z, n, k, 128, x, rows=rows)
     assert_parity(got, yr, gemv_tol(S, yr), f"int4 n{n} k{k} b{batch}")
+
+
+@pytest.mark.parametrize("k", [512, 5120])
+def test_int4_gemv_unaligned_x(dev, k):
+    """x two bytes past a 16-byte boundary takes the element-load instantiation."""
+    n = 48
+    q, s, z, packed, x = _int4_case(dev, n, k, 1, layer=3)
+    xb = dev_bf16(x, dev).reshape(-1)
+    buf = torch.zeros(k + 8, dtype=xb.dtype, device=dev)
+    buf[1:k + 1] = xb
+    xv = buf[1:k + 1].view(1, k)
+    assert xv.data_ptr() % 16 == 2
+    got = to_np(tt.int4_gemv(packed, n, k, xv))
+    yr, S = oracle.int4_gemv(q, s, z, n, k, 128, x)
+    assert_parity(got, yr, gemv_tol(S, yr), f"int4 unaligned x k{k}")
 
 
 def test_int4_dequantize_bit_exact(dev):
