@@ -14,6 +14,8 @@
 //  2. k_attn_combine, one wave per (query head, 64 output columns): rescales
 //     the chunks to the global maximum and sums them in chunk order (fixed
 //     order: the result is the same on every run).
+// A context of at most 256 / D chunks runs as one launch instead: one
+// workgroup per kv head, one wave per chunk, merged through LDS.
 #include "device.h"
 #include "tt_internal.h"
 
@@ -24,6 +26,10 @@ namespace tt {
 #endif
 constexpr int kAttnChunk = TT_ATTN_CHUNK;  // positions per chunk (a multiple of 32)
 constexpr int kAttnOob = 0x7FFFFF00;
+// A context of at most 256 / D chunks (64 KiB of keys and values per kv
+// head) takes one workgroup of that many waves per kv head and no combine;
+// longer contexts split over one-wave workgroups.
+template <int D> constexpr int attn_single_waves() { return 256 / D; }
 
 struct AttnArgs {
     const uint16_t *q, *k, *v;  // q [hq][d]; k, v [hkv][tcap][d]
@@ -62,17 +68,26 @@ __device__ __forceinline__ int attn_swz(int r) {
     return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
 }
 
-template <int D, int G, int NB>
-__global__ __launch_bounds__(64) void k_attn_partial(AttnArgs a) {
+// W = 1: one wave per (chunk, kv head), partials to the workspace for the
+// combine.  W > 1 (contexts of at most W chunks): one workgroup of W waves per
+// kv head, wave w taking chunk w; waves 1 .. W-1 hand (max, sum, P V) to wave
+// 0 through LDS, which rescales each part to the common maximum, adds them in
+// wave order and writes the normalised output -- one launch for the call.
+template <int D, int G, int NB, int W>
+__global__ __launch_bounds__(64 * W) void k_attn_partial(AttnArgs a) {
     static_assert(NB % 2 == 0, "blocks of 16 positions come in pairs");
     constexpr int KK = D / 32;           // score steps over d
     constexpr int CPR = D / 8;           // 16-byte chunks per V row
     constexpr int NV = 16 * NB * CPR / 64;  // V DMA instructions
     constexpr int NT = D / 16;           // output column tiles
-    __shared__ __attribute__((aligned(16))) uint16_t s_v[16 * NB * D];
-    const int lane = threadIdx.x;
+    __shared__ __attribute__((aligned(16))) uint16_t s_vw[W][16 * NB * D];
+    __shared__ f32x4_t s_o[W > 1 ? W - 1 : 1][W > 1 ? NT : 1][64];
+    __shared__ float s_ml[W][2][16];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    uint16_t *s_v = s_vw[wave];
     const int c = blockIdx.x, g = blockIdx.y;
-    const int t0 = c * 16 * NB;
+    const int t0 = (c * W + wave) * 16 * NB;
     const int col = lane & 15, grp = lane >> 4;
 
     const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
@@ -137,14 +152,16 @@ __global__ __launch_bounds__(64) void k_attn_partial(AttnArgs a) {
     }
 
     // 3. p = exp2(s - max) (0 past T), its sum, and the hi / lo A operands
-    //    (the chunk starts below T, so the maximum is finite)
+    //    (a chunk of the split starts below T; a wave of a single workgroup
+    //    whose positions all lie past T has max -inf and takes p = 0)
+    const float mref = (W > 1 && m == -INFINITY) ? 0.0f : m;
     float l = 0.0f;
     bf16x8_t ph[NB / 2], pl[NB / 2];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float p = __builtin_amdgcn_exp2f(sc[b][r] - m);
+            const float p = __builtin_amdgcn_exp2f(sc[b][r] - mref);
             l += p;
             const __bf16 hi = (__bf16)p;
             ph[b / 2][(b & 1) * 4 + r] = hi;
@@ -177,6 +194,44 @@ __global__ __launch_bounds__(64) void k_attn_partial(AttnArgs a) {
             o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[mm], vb, o[dt], 0, 0, 0);
             o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[mm], vb, o[dt], 0, 0, 0);
         }
+    }
+
+    if constexpr (W > 1) {
+        // 5'. single workgroup: merge the waves in LDS and write the output
+        if (lane < 16) {
+            s_ml[wave][0][lane] = m;
+            s_ml[wave][1][lane] = l;
+        }
+        if (wave > 0)
+#pragma unroll
+            for (int dt = 0; dt < NT; ++dt) s_o[wave - 1][dt][lane] = o[dt];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        if (wave > 0) return;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int head = 4 * grp + r;
+            float M = s_ml[0][0][head];
+#pragma unroll
+            for (int w = 1; w < W; ++w) M = fmaxf(M, s_ml[w][0][head]);
+            float L = 0.0f, f[W];
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                f[w] = __builtin_amdgcn_exp2f(s_ml[w][0][head] - M);  // 0 for an empty wave
+                L = fmaf(s_ml[w][1][head], f[w], L);
+            }
+#pragma unroll
+            for (int dt = 0; dt < NT; ++dt) {
+                float v = o[dt][r] * f[0];
+#pragma unroll
+                for (int w = 1; w < W; ++w) v = fmaf(s_o[w - 1][dt][lane][r], f[w], v);
+                if (head < G)
+                    store_out(a.out, (int64_t)(g * G + head) * D + dt * 16 + col, v / L,
+                              a.out_bf16);
+            }
+        }
+        return;
     }
 
     // 5. the chunk's partial sums: lane (column c, group q) holds heads
@@ -274,7 +329,11 @@ int64_t attn_chunks(int64_t T) { return ceil_div(T, kAttnChunk); }
 
 template <int D, int G>
 tt_status launch_attn(const AttnArgs &a, hipStream_t s) {
-    TT_TRY(launch("gqa attention (chunks)", k_attn_partial<D, G, kAttnChunk / 16>,
+    constexpr int W = attn_single_waves<D>();
+    if (a.nchunks <= W)
+        return launch("gqa attention (single workgroup)", k_attn_partial<D, G, kAttnChunk / 16, W>,
+                      dim3(1u, (unsigned)a.hkv), dim3(64 * W), 0, s, a);
+    TT_TRY(launch("gqa attention (chunks)", k_attn_partial<D, G, kAttnChunk / 16, 1>,
                   dim3((unsigned)a.nchunks, (unsigned)a.hkv), dim3(64), 0, s, a));
     return launch("gqa attention (combine)", k_attn_combine<D, G>,
                   dim3((unsigned)a.hq, (unsigned)(D / 64)), dim3(64), 0, s, a);

@@ -44,7 +44,9 @@ def _case(dev, hq, hkv, d, tcap, T, seed, out_dtype=torch.float32, q_mul=1.0, k_
                                         (40, 10, 128, 4096), (64, 8, 64, 100),
                                         (64, 8, 64, 2049), (8, 8, 128, 300), (4, 2, 64, 65),
                                         (32, 4, 128, 517), (16, 16, 64, 33), (16, 8, 128, 1),
-                                        (32, 8, 64, 4097), (8, 4, 64, 16), (16, 2, 128, 8192)])
+                                        (32, 8, 64, 4097), (8, 4, 64, 16), (16, 2, 128, 8192),
+                                        (40, 10, 128, 128), (8, 2, 128, 100), (64, 8, 64, 256),
+                                        (16, 8, 64, 193)])
 def test_gqa_attention(dev, hq, hkv, d, T):
     got, ref, tol = _case(dev, hq, hkv, d, T, T, hq * 7 + T)
     assert_parity(got, ref, tol, f"attention hq{hq} hkv{hkv} d{d} T{T}")
@@ -63,13 +65,20 @@ def test_gqa_attention_spare_capacity_and_bf16_out(dev):
     assert_parity(got, ref, tol, "attention tcap 1000 T 777 bf16 out")
 
 
+def test_gqa_attention_single_workgroup_bf16_out(dev):
+    # a context that fits one workgroup per kv head, in a larger cache
+    got, ref, tol = _case(dev, 64, 8, 64, 600, 230, 11, out_dtype=torch.bfloat16)
+    assert_parity(got, ref, tol, "attention tcap 600 T 230 bf16 out (one workgroup)")
+
+
 def test_gqa_attention_run_to_run_identical(dev):
     gen = np.random.default_rng(9)
     hq, hkv, d, T = 40, 10, 128, 1500
     q = dev_bf16(workloads.bf16_bits(gen.standard_normal((hq, d)).astype(np.float32)), dev)
     K = dev_bf16(workloads.bf16_bits(gen.standard_normal((hkv, T, d)).astype(np.float32)), dev)
     V = dev_bf16(workloads.bf16_bits(gen.standard_normal((hkv, T, d)).astype(np.float32)), dev)
-    a = tt.gqa_attention_decode(q, K, V, hq, hkv, d, T, 0.088)
-    b = tt.gqa_attention_decode(q, K, V, hq, hkv, d, T, 0.088)
-    torch.cuda.synchronize()
-    assert torch.equal(a, b)
+    for t in (T, 100):   # split over chunks, and one workgroup per kv head
+        a = tt.gqa_attention_decode(q, K, V, hq, hkv, d, t, 0.088)
+        b = tt.gqa_attention_decode(q, K, V, hq, hkv, d, t, 0.088)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
