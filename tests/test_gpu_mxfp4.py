@@ -119,6 +119,16 @@ def test_smollm3_layer0_every_row(dev):
     assert_parity(got, ref["h"], h_tol(ref), "smollm3 layer 0 all rows")
 
 
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_many_tiles_every_row(dev, out_dtype):
+    """More tiles than the chip holds at once at K = 5120 (1125 ten-wave
+    tiles), every row checked."""
+    w = workloads.Workload(9, "wide", 5120, 9000)
+    got, ref = _gateup_case(dev, w, 0, 1, out_dtype=out_dtype)
+    assert_parity(got, ref["h"], h_tol(ref, bf16=out_dtype == torch.bfloat16),
+                  f"h5120 i9000 {out_dtype}")
+
+
 def test_phi4_gateup_sampled_rows(dev):
     w = workloads.PHI4
     rows = _sample_rows(w.inter, 256, 1)
