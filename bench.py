@@ -126,24 +126,37 @@ def time_graph(torch, graph, steps, warmup):
 
 def cpu_baseline_gateup(w, seconds):
     """The oracle, untuned, single-threaded, on full layers of the same
-    workload until about `seconds` of CPU work."""
+    workload until about `seconds` of CPU work; then the OpenMP build of the
+    same loops (rows split over the host threads, same bits) on the same
+    layers for about a third of that."""
     import oracle
     import workloads
-    t_total, calls, nbytes = 0.0, 0, 0
-    layer = 0
-    while t_total < seconds and layer < w.layers:
-        g, u = workloads.gateup(w, layer)
-        x = workloads.activations(w.wid, layer, 1, w.hidden)
-        t0 = time.perf_counter()
-        oracle.mxfp4_gateup_swiglu(g, u, w.inter, w.hidden, x)
-        t_total += time.perf_counter() - t0
-        calls += 1
-        nbytes += gateup_bytes(w.inter, w.hidden, 1)
-        layer += 1
+
+    def timed(parallel, budget):
+        t_total, calls, nbytes, layer = 0.0, 0, 0, 0
+        while t_total < budget and layer < w.layers:
+            g, u = workloads.gateup(w, layer)
+            x = workloads.activations(w.wid, layer, 1, w.hidden)
+            t0 = time.perf_counter()
+            oracle.mxfp4_gateup_swiglu(g, u, w.inter, w.hidden, x, parallel=parallel)
+            t_total += time.perf_counter() - t0
+            calls += 1
+            nbytes += gateup_bytes(w.inter, w.hidden, 1)
+            layer += 1
+        return t_total, calls, nbytes
+
+    t_total, calls, nbytes = timed(False, seconds)
+    tp, cp, bp = timed(True, seconds / 3)
+    nthr = oracle.threads(parallel=True)
     return dict(value=round(nbytes / t_total / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
                 us_per_call=round(t_total / calls * 1e6, 1),
                 sample=f"{calls} full {w.name} layer calls (batch 1), single thread, "
-                       f"fp64 oracle, {t_total:.1f} s")
+                       f"fp64 oracle, {t_total:.1f} s",
+                parallel=dict(value=round(bp / tp / 1e9, 4), unit="GB/s", cores=nthr,
+                              us_per_call=round(tp / cp * 1e6, 1),
+                              sample=f"{cp} full {w.name} layer calls, the same oracle loops "
+                                     f"with rows split over {nthr} OpenMP threads, "
+                                     f"{tp:.1f} s"))
 
 
 def run(args):

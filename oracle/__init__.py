@@ -25,31 +25,41 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# the same source with its row loops split over OpenMP threads, for the
+# benchmark's CPU timing only (the parity tests use the plain build)
+_LIB_OMP = os.path.join(_HERE, "liboracle_omp.so")
 
 # Plain build: no fast-math, no vector intrinsics, default rounding mode.
 GCC_CMD = ["gcc", "-std=c99", "-O2", "-fno-fast-math", "-ffp-contract=off",
            "-fPIC", "-shared", _SRC, "-o", _LIB, "-lm"]
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so (gcc) and return its path."""
-    if force or not os.path.exists(_LIB) or \
-            os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp"
-        cmd = GCC_CMD[:-3] + ["-o", tmp, "-lm"]
+def _build_one(path: str, extra, force: bool) -> str:
+    if force or not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+        tmp = path + ".tmp"
+        cmd = GCC_CMD[:-3] + list(extra) + ["-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, path)
+    return path
 
 
-_lib = None
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so (and the OpenMP timing build
+    liboracle_omp.so) with gcc; returns the plain library's path."""
+    _build_one(_LIB_OMP, ["-fopenmp"], force)
+    return _build_one(_LIB, [], force)
 
 
-def lib() -> ctypes.CDLL:
-    global _lib
-    if _lib is None:
-        build(force=False)
-        L = ctypes.CDLL(_LIB)
+_libs = {}
+
+
+def lib(parallel: bool = False) -> ctypes.CDLL:
+    if parallel not in _libs:
+        if parallel:
+            _build_one(_LIB_OMP, ["-fopenmp"], False)
+        else:
+            build(force=False)
+        L = ctypes.CDLL(_LIB_OMP if parallel else _LIB)
         P, I64, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_double
         sig = {
             "or_e2m1_value": (D, [ctypes.c_int]),
@@ -75,13 +85,19 @@ def lib() -> ctypes.CDLL:
             "or_int4_quantize": (ctypes.c_int, [P, I64, I64, I64, P, P, P]),
             "or_int4_dequantize": (None, [P, P, P, I64, I64, I64, P]),
             "or_int4_gemv": (None, [P, P, P, I64, I64, I64, P, I64, P, I64, P, P]),
+            "or_threads": (ctypes.c_int, []),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
-        _lib = L
-    return _lib
+        _libs[parallel] = L
+    return _libs[parallel]
+
+
+def threads(parallel: bool = False) -> int:
+    """Threads the oracle's row loops use (1 for the plain build)."""
+    return int(lib(parallel).or_threads())
 
 
 def _p(a):
@@ -151,15 +167,16 @@ def mxfp4_gemv(codes, scales, ps, n, k, x_bf16, rows=None):
     return y, S
 
 
-def mxfp4_gateup_swiglu(g, u, inter, hidden, x_bf16, rows=None):
+def mxfp4_gateup_swiglu(g, u, inter, hidden, x_bf16, rows=None, parallel=False):
     """g and u are (codes, scales, ps) triples.  Returns a dict with h, g,
-    u, Sg, Su, each [batch][nrows] fp64."""
+    u, Sg, Su, each [batch][nrows] fp64.  parallel=True runs the OpenMP
+    timing build of the same loops (same bits)."""
     gc, gs, gp = _c(g[0], np.uint8), _c(g[1], np.uint8), _c(g[2], np.float32)
     uc, us, up = _c(u[0], np.uint8), _c(u[1], np.uint8), _c(u[2], np.float32)
     x = _c(x_bf16, np.uint16).reshape(-1, hidden)
     r, nr = _rows(rows, inter)
     out = {k: np.empty((x.shape[0], nr)) for k in ("h", "g", "u", "Sg", "Su")}
-    lib().or_mxfp4_gateup_swiglu(_p(gc), _p(gs), _p(gp), _p(uc), _p(us), _p(up),
+    lib(parallel).or_mxfp4_gateup_swiglu(_p(gc), _p(gs), _p(gp), _p(uc), _p(us), _p(up),
                                  inter, hidden, _p(x), x.shape[0], _p(r), nr,
                                  _p(out["h"]), _p(out["g"]), _p(out["u"]),
                                  _p(out["Sg"]), _p(out["Su"]))

@@ -56,6 +56,9 @@
  * logits; the routing weight multiplies each expert's down output; INT4 is
  * w = s*(q - z) over groups of consecutive k with a partial last group.
  */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -190,26 +193,47 @@ void or_mxfp4_gemv(const uint8_t *codes, const uint8_t *scales,
                    const int64_t *rows, int64_t nrows,
                    double *y, double *S)
 {
-    float *w = (float *)malloc(sizeof(float) * (size_t)k);
     (void)n;
-    for (int64_t i = 0; i < nrows; ++i) {
-        int64_t r = rows ? rows[i] : i;
-        double p = ps ? (double)ps[r] : 1.0;
-        decode_mxfp4_row(codes, scales, k, r, w);
-        for (int64_t b = 0; b < batch; ++b) {
-            const uint16_t *xb = x + b * k;
-            double acc = 0.0, mag = 0.0;
-            for (int64_t j = 0; j < k; ++j) {
-                double t = (double)w[j] * or_bf16_value(xb[j]);
-                acc += t;
-                mag += fabs(t);
+    /* Rows are independent; the timing build (-fopenmp) splits them over
+     * threads, each row's sum keeping the same order, so both builds give
+     * the same bits.  The plain build ignores the pragmas. */
+#ifdef _OPENMP
+#pragma omp parallel
+#endif
+    {
+        float *w = (float *)malloc(sizeof(float) * (size_t)k);
+#ifdef _OPENMP
+#pragma omp for schedule(static)
+#endif
+        for (int64_t i = 0; i < nrows; ++i) {
+            int64_t r = rows ? rows[i] : i;
+            double p = ps ? (double)ps[r] : 1.0;
+            decode_mxfp4_row(codes, scales, k, r, w);
+            for (int64_t b = 0; b < batch; ++b) {
+                const uint16_t *xb = x + b * k;
+                double acc = 0.0, mag = 0.0;
+                for (int64_t j = 0; j < k; ++j) {
+                    double t = (double)w[j] * or_bf16_value(xb[j]);
+                    acc += t;
+                    mag += fabs(t);
+                }
+                y[b * nrows + i] = p * acc;
+                if (S)
+                    S[b * nrows + i] = fabs(p) * mag;
             }
-            y[b * nrows + i] = p * acc;
-            if (S)
-                S[b * nrows + i] = fabs(p) * mag;
         }
+        free(w);
     }
-    free(w);
+}
+
+/* Threads the loops above run on (1 in the plain build). */
+int or_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }
 
 /* silu(z) = z * sigmoid(z) = z / (1 + e^-z)  ([DL2] gated activation). */

@@ -58,6 +58,19 @@ def test_gateup_up_scale_doubling_doubles_h():
     assert np.array_equal(b["g"], a["g"])
 
 
+def test_gateup_openmp_timing_build_gives_the_same_bits():
+    """The benchmark times an OpenMP build of the same row loops: every
+    output, magnitude and partial must match the plain build bit for bit."""
+    w = workloads.Workload(9, "omp", 512, 300)
+    g, u = workloads.gateup(w, 0)
+    x = workloads.activations(w.wid, 0, 2, w.hidden)
+    a = oracle.mxfp4_gateup_swiglu(g, u, w.inter, w.hidden, x)
+    b = oracle.mxfp4_gateup_swiglu(g, u, w.inter, w.hidden, x, parallel=True)
+    assert oracle.threads() == 1
+    for k in a:
+        assert np.array_equal(a[k].view(np.uint64), b[k].view(np.uint64)), k
+
+
 def test_route_topk_matches_stable_sort_and_softmax():
     gen = np.random.default_rng(0)
     for trial in range(50):
