@@ -300,7 +300,7 @@ def run(args):
                                   routing="a distinct seeded routing per layer, fused into "
                                           "the expert gate/up call",
                                   launch="one HIP graph per step"),
-                      roofline=dict(bound="hbm", kernel="k_gateup_mx(routed)+k_down_combine",
+                      roofline=dict(bound="hbm", kernel="k_gateup_mx(routed)+k_down_mx",
                                     achieved=round(gbs, 2), peak=PEAK_HBM_GBS, unit="GB/s",
                                     frac=round(gbs / PEAK_HBM_GBS, 4),
                                     traffic=profiled_traffic(
