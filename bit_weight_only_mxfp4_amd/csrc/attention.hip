@@ -50,16 +50,18 @@ typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 
 // Chunk pass, one wave per (16 NB positions, kv head).  Scores: S = K Q^T
 // on v_mfma_f32_16x16x32_bf16 per block of 16 positions, A = the key rows
-// (lane l: position l % 16, d = 32 kk + 8 (l / 16) .. +7: one 16-byte load),
+// (lane l: position l % 16, d = 32 kk + 8 (l / 16) .. +7: one 16-byte LDS
+// read),
 // B = the G query heads of the kv head as columns (heads past G are zero
 // columns); lane (head c, group q) gets positions 4q .. 4q+3 of the block.
 // The wave's maximum per head and p = exp2(s - max) stay in that layout,
 // which is the A layout of the next product: P V on the same instruction
 // with 32 positions per step (block 2m in elements 0..3, block 2m+1 in
 // 4..7), P split into bf16 hi + lo parts (p - hi is exact in fp32 and its
-// bf16 rounding leaves a 2^-18 relative residue) and V as B.  V goes to LDS
-// by buffer->LDS DMA in its row-major layout with the 16-byte chunks of row
-// r xor-swizzled, and comes back as B operands through ds_read_b64_tr_b16:
+// bf16 rounding leaves a 2^-18 relative residue) and V as B.  K and V go to
+// LDS by buffer->LDS DMA (contiguous 1 KiB per instruction) in their
+// row-major layout with the 16-byte chunks of row r xor-swizzled; K comes
+// back by plain 16-byte reads, V as B operands through ds_read_b64_tr_b16:
 // within each group of 16 lanes, source lane 4j + a addresses row j,
 // columns 4a .. 4a+3 of a 4 x 16 tile, and lane i receives column i, rows
 // 0..3.  No barrier across waves and no cross-lane reduction of P V.
@@ -80,12 +82,13 @@ __global__ __launch_bounds__(64 * W) void k_attn_partial(AttnArgs a) {
     constexpr int CPR = D / 8;           // 16-byte chunks per V row
     constexpr int NV = 16 * NB * CPR / 64;  // V DMA instructions
     constexpr int NT = D / 16;           // output column tiles
+    __shared__ __attribute__((aligned(16))) uint16_t s_kw[W][16 * NB * D];
     __shared__ __attribute__((aligned(16))) uint16_t s_vw[W][16 * NB * D];
     __shared__ f32x4_t s_o[W > 1 ? W - 1 : 1][W > 1 ? NT : 1][64];
     __shared__ float s_ml[W][2][16];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    uint16_t *s_v = s_vw[wave];
+    uint16_t *s_k = s_kw[wave], *s_v = s_vw[wave];
     const int c = blockIdx.x, g = blockIdx.y;
     const int t0 = (c * W + wave) * 16 * NB;
     const int col = lane & 15, grp = lane >> 4;
@@ -98,18 +101,19 @@ __global__ __launch_bounds__(64 * W) void k_attn_partial(AttnArgs a) {
     const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(a.v + head_off), 0, a.T * D * 2, 0x00020000);
 
-    // 1. query columns, key rows, then V into LDS (rows past T read zeros)
+    // 1. query columns from memory; the chunk's key rows, then its value
+    //    rows, into LDS by DMA (rows past T read zeros)
     uint4 qb[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
         qb[kk] = attn_load16(qr, col < G ? (col * D + 32 * kk + 8 * grp) * 2 : kAttnOob);
-    uint4 ka[NB][KK];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        const int t = t0 + 16 * b + col;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            ka[b][kk] = attn_load16(kr, t < a.T ? (t * D + 32 * kk + 8 * grp) * 2 : kAttnOob);
+    for (int u = 0; u < NV; ++u) {
+        const int L = u * 64 + lane, r = L / CPR, x = (L % CPR) ^ attn_swz<D>(r);
+        const int t = t0 + r;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            kr, (__attribute__((address_space(3))) void *)(s_k + u * 512), 16,
+            t < a.T ? (t * D + 8 * x) * 2 : kAttnOob, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
@@ -120,6 +124,18 @@ __global__ __launch_bounds__(64 * W) void k_attn_partial(AttnArgs a) {
             t < a.T ? (t * D + 8 * x) * 2 : kAttnOob, 0, 0, 0);
     }
 
+    __builtin_amdgcn_sched_barrier(0);  // every DMA issued before the first read
+    // key rows back as A operands: lane l takes row 16 b + l % 16 at d chunk
+    // 4 kk + l / 16
+    uint4 ka[NB][KK];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const int r = 16 * b + col, X = 4 * kk + grp;
+            ka[b][kk] = *reinterpret_cast<const uint4 *>(
+                reinterpret_cast<const char *>(s_k) + (r * CPR + (X ^ attn_swz<D>(r))) * 16);
+        }
     // 2. scores in base-2 units, -inf past T; the wave's maximum per head
     f32x4_t sc[NB];
 #pragma unroll
