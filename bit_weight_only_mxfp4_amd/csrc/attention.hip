@@ -292,35 +292,39 @@ __device__ __forceinline__ float wave_reduce(float v) {
 __device__ __forceinline__ float wave_max(float v) { return wave_reduce<true>(v); }
 __device__ __forceinline__ float wave_sum(float v) { return wave_reduce<false>(v); }
 
-// One wave per (query head h = g * G + i, 64 output columns): lane k takes
-// chunk c0 + k's (max, sum) and the wave maximum gives every chunk's factor
-// exp2(m_c - M); lane e accumulates column e over the chunks of the round
-// with each factor read from its chunk's lane (v_readlane), in four
-// interleaved partial sums added in a fixed order.  Rounds of 64 chunks
-// rescale the running sums to the new maximum.  No LDS and no barrier.
+// One wave per (query head h = g * G + i, 64 output columns).  Rounds of 64
+// chunks: lane k takes chunk c0 + k's (max, sum), and the wave maximum gives
+// every chunk's factor exp2(m_c - M); lane (phase c, column group q) takes
+// columns 4q .. 4q+3 of chunks 4u + c (16-byte loads: one instruction
+// covers four chunks x 64 columns, all issued before the first use), gets
+// each chunk's factor from the chunk's lane by ds_bpermute, and the four
+// phases are added in a fixed order (lane pairs 16 apart, then 32 apart).
+// Each round rescales the running sums to the new maximum.  No LDS and no
+// barrier.
 template <int D, int G>
 __global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
     const int h = blockIdx.x, lane = threadIdx.x;
     const int g = h / G, i = h - g * G;
-    const int e = blockIdx.y * 64 + lane;
+    const int e0 = blockIdx.y * 64 + (lane & 15) * 4, ph = lane >> 4;
     const int nc = a.nchunks;
     const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
         a.part + (int64_t)g * nc * G * D, 0, nc * G * D * 4, 0x00020000);
     const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(
         a.ml + (int64_t)g * nc * G * 2, 0, nc * G * 2 * 4, 0x00020000);
-    float M = -INFINITY, L = 0.0f, o = 0.0f;
+    float M = -INFINITY, L = 0.0f, o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int c0 = 0; c0 < nc; c0 += 64) {
         const int n = min(64, nc - c0);
         const f32x2_t ml = __builtin_bit_cast(
             f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
                          mr, lane < n ? ((c0 + lane) * G + i) * 8 : kAttnOob, 0, 0));
-        float pv[64];
+        f32x4_t pv[16];
 #pragma unroll
-        for (int u = 0; u < 64; ++u)
-            pv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                  pr, u < n ? ((c0 + u) * G + i) * D * 4 + e * 4
-                                                            : kAttnOob, 0, 0));
-        // every load of the round is issued before the first use of any
+        for (int u = 0; u < 16; ++u) {
+            const int cu = 4 * u + ph;
+            pv[u] = __builtin_bit_cast(
+                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                             pr, cu < n ? (((c0 + cu) * G + i) * D + e0) * 4 : kAttnOob, 0, 0));
+        }
         __builtin_amdgcn_sched_barrier(0);
         const float m = lane < n ? ml.x : -INFINITY;
         const float Mn = fmaxf(M, wave_max(m));
@@ -329,14 +333,19 @@ __global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
         L = fmaf(L, r, wave_sum(lane < n ? ml.y * f : 0.0f));
         float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int u = 0; u < 64; ++u)
-            acc[u & 3] = fmaf(pv[u], __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                                  __builtin_bit_cast(int, f), u)),
-                              acc[u & 3]);
-        o = fmaf(o, r, (acc[0] + acc[1]) + (acc[2] + acc[3]));
+        for (int u = 0; u < 16; ++u) {
+            const float fu = __builtin_bit_cast(
+                float, __builtin_amdgcn_ds_bpermute((4 * u + ph) * 4, __builtin_bit_cast(int, f)));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = fmaf(pv[u][j], fu, acc[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = fmaf(o[j], r, sum_xor32(sum_xor16(acc[j])));
         M = Mn;
     }
-    store_out(a.out, (int64_t)h * D + e, o / L, a.out_bf16);
+    if (ph == 0)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) store_out(a.out, (int64_t)h * D + e0 + j, o[j] / L, a.out_bf16);
 }
 
 namespace {
