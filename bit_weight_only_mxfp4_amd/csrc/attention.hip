@@ -15,7 +15,8 @@
 //     the chunks to the global maximum and sums them in chunk order (fixed
 //     order: the result is the same on every run).
 // A context of at most 256 / D chunks runs as one launch instead: one
-// workgroup per kv head, one wave per chunk, merged through LDS.
+// workgroup per kv head, one wave per chunk, merged through LDS.  Chunks are
+// 64 positions, 32 for the split at contexts up to 2048.
 #include "device.h"
 #include "tt_internal.h"
 
@@ -350,16 +351,32 @@ __global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
 
 namespace {
 
-int64_t attn_chunks(int64_t T) { return ceil_div(T, kAttnChunk); }
+// Positions per chunk: kAttnChunk for the one-launch path and for long
+// contexts; half of it for the split at mid contexts (at most kAttnMidT
+// positions), where twice the workgroups fill the chip better than the
+// extra partials cost (measured crossover between 2048 and 4096).
+constexpr int64_t kAttnMidT = 2048;
+int attn_chunk(int64_t d, int64_t T) {
+    const bool single = ceil_div(T, kAttnChunk) <= 256 / d;
+    return (!single && T <= kAttnMidT) ? kAttnChunk / 2 : kAttnChunk;
+}
+
+int64_t attn_chunks(int64_t d, int64_t T) { return ceil_div(T, attn_chunk(d, T)); }
 
 template <int D, int G>
 tt_status launch_attn(const AttnArgs &a, hipStream_t s) {
     constexpr int W = attn_single_waves<D>();
-    if (a.nchunks <= W)
-        return launch("gqa attention (single workgroup)", k_attn_partial<D, G, kAttnChunk / 16, W>,
+    constexpr int NB = kAttnChunk / 16;
+    const bool full = attn_chunk(D, a.T) == kAttnChunk;
+    if (full && a.nchunks <= W)
+        return launch("gqa attention (single workgroup)", k_attn_partial<D, G, NB, W>,
                       dim3(1u, (unsigned)a.hkv), dim3(64 * W), 0, s, a);
-    TT_TRY(launch("gqa attention (chunks)", k_attn_partial<D, G, kAttnChunk / 16, 1>,
-                  dim3((unsigned)a.nchunks, (unsigned)a.hkv), dim3(64), 0, s, a));
+    if (full)
+        TT_TRY(launch("gqa attention (chunks)", k_attn_partial<D, G, NB, 1>,
+                      dim3((unsigned)a.nchunks, (unsigned)a.hkv), dim3(64), 0, s, a));
+    else
+        TT_TRY(launch("gqa attention (chunks)", k_attn_partial<D, G, NB / 2, 1>,
+                      dim3((unsigned)a.nchunks, (unsigned)a.hkv), dim3(64), 0, s, a));
     return launch("gqa attention (combine)", k_attn_combine<D, G>,
                   dim3((unsigned)a.hq, (unsigned)(D / 64)), dim3(64), 0, s, a);
 }
@@ -397,7 +414,7 @@ extern "C" int64_t tt_gqa_attention_workspace_bytes(int64_t hq, int64_t hkv, int
                                                     int64_t T) {
     tt_status st = check_attn_shape(hq, hkv, d, T);
     if (st != TT_OK) return st;
-    return hq * attn_chunks(T) * (d + 2) * 4;
+    return hq * attn_chunks(d, T) * (d + 2) * 4;
 }
 
 extern "C" tt_status tt_gqa_attention_decode(const void *q, const void *k_cache,
@@ -432,7 +449,7 @@ extern "C" tt_status tt_gqa_attention_decode(const void *q, const void *k_cache,
     a.hkv = (int32_t)hkv;
     a.tcap = (int32_t)tcap;
     a.T = (int32_t)T;
-    a.nchunks = (int32_t)attn_chunks(T);
+    a.nchunks = (int32_t)attn_chunks(d, T);
     a.scale2 = scale * 1.4426950408889634f;
     const int64_t G = hq / hkv;
     a.part = static_cast<float *>(workspace);
