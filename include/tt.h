@@ -303,10 +303,14 @@ tt_status tt_fp8_gemv(const void *w_packed, int64_t n, int64_t k, const void *x,
  * ((g * tcap) + t) * d, T <= tcap (all device memory, 16-byte aligned);
  * d is 64 or 128; hq / hkv is 1, 2, 4 or 8; out [hq][d] of out_dtype.
  * workspace: device memory of at least tt_gqa_attention_workspace_bytes
- * bytes for the per-chunk partial results (64 positions per chunk); it
+ * bytes for the per-chunk partial results (hq x chunks x (d + 2) floats;
+ * chunks of 32 positions for 256 / d * 64 < T <= 2048, of 64 otherwise); it
  * needs no initialisation, its contents are overwritten, and calls that
- * share one workspace must not overlap.  Scores, exponentials and sums in
- * fp32; the chunks are combined in a fixed order.  Two kernel launches.
+ * share one workspace must not overlap.  Scores are bf16 x bf16 products
+ * summed in fp32, the softmax weights enter the value sum as two bf16
+ * parts, exponentials and sums are fp32, and the chunks are combined in a
+ * fixed order (the same bits on every run).  One kernel launch when T <=
+ * 256 / d * 64 (one workgroup per kv head), two otherwise.
  */
 int64_t tt_gqa_attention_workspace_bytes(int64_t hq, int64_t hkv, int64_t d, int64_t T);
 tt_status tt_gqa_attention_decode(const void *q, const void *k_cache, const void *v_cache,

@@ -268,7 +268,15 @@ def test_attention_validation():
     f = tt.lib.tt_gqa_attention_decode
     ok = dict(hq=40, hkv=10, d=128, tcap=512, T=300)
     need = tt.gqa_attention_workspace_bytes(40, 10, 128, 300)
-    assert need == 40 * 5 * 130 * 4
+    # hq x chunks x (d + 2) floats; chunks of 32 positions for the split up
+    # to T = 2048, of 64 above it and for the one-launch path (at most
+    # 256 / d chunks of 64), which still reports the split's size
+    assert need == 40 * 10 * 130 * 4
+    assert tt.gqa_attention_workspace_bytes(40, 10, 128, 2048) == 40 * 64 * 130 * 4
+    assert tt.gqa_attention_workspace_bytes(40, 10, 128, 2049) == 40 * 33 * 130 * 4
+    assert tt.gqa_attention_workspace_bytes(40, 10, 128, 100) == 40 * 2 * 130 * 4
+    assert tt.gqa_attention_workspace_bytes(64, 8, 64, 256) == 64 * 4 * 66 * 4
+    assert tt.gqa_attention_workspace_bytes(64, 8, 64, 257) == 64 * 9 * 66 * 4
     def call(hq=40, hkv=10, d=128, tcap=512, T=300, ws=need, dt=0, ptr=P):
         return f(ptr, P, P, hq, hkv, d, tcap, T, 0.1, P, dt, P, ws, None)
     assert call(hq=30) == -2              # not a multiple
