@@ -151,6 +151,14 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Orders one wave's own LDS writes before its later LDS reads, with no
+// workgroup barrier.
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
 // Scaled-MFMA path (batch 1 and 2 and the routed slots): each packed unit
 // and its E8M0 scale byte go to v_mfma_scale_f32_16x16x128_f8f6f4 as loaded
 // (layouts and the two-part E4M3 activations: device.h).  Token t's hi part
@@ -203,14 +211,30 @@ __global__ __launch_bounds__(1024) void k_gateup_mx(GateUpArgs a) {
     const int tok0 = routed ? slot / a.topk : slot * NTOK;   // first token of the workgroup
     const int ntok = routed ? 1 : min(NTOK, a.batch - tok0);
 
-    // 1. activations: 16-byte chunks, NTOK * kp / 8 of them (zero past K
-    //    and past the batch); chunk i of a token is elements 8i .. 8i+7
+    // 1. activations: 16-byte chunks (zero past K and past the batch);
+    //    chunk i of a token is elements 8i .. 8i+7.  One-tile workgroups:
+    //    each wave fetches only the UPW * 16 chunks per token that its own
+    //    units read (chunk part * UPW * 16 + 64 c + lane), and stages them in
+    //    its own part of LDS.  Otherwise the tiles of the workgroup share
+    //    one staging of all NTOK * kp / 8 chunks behind a barrier.
+    constexpr bool kOwnX = TPB == 1;
     constexpr int XC = NTOK * UPW / 4;   // >= chunks per thread (nthreads >= 64 ks)
     const int tchunks = L.kp / 8, xvalid = a.hidden / 8;
+    const auto xchunk = [&](int j, int &t, int &ci) {
+        if (kOwnX) {
+            t = j / (UPW / 4);
+            ci = part * UPW * 16 + (j % (UPW / 4)) * 64 + lane;
+        } else {
+            const int idx = tid + j * nthreads;
+            t = idx / tchunks;
+            ci = idx - t * tchunks;
+        }
+    };
     uint4 xv[XC];
 #pragma unroll
     for (int j = 0; j < XC; ++j) {
-        const int idx = tid + j * nthreads, t = idx / tchunks, ci = idx - t * tchunks;
+        int t, ci;
+        xchunk(j, t, ci);
         xv[j] = (t < ntok && ci < xvalid)
                     ? reinterpret_cast<const uint4 *>(a.x + (int64_t)(tok0 + t) * a.hidden)[ci]
                     : make_uint4(0, 0, 0, 0);
@@ -286,7 +310,8 @@ __global__ __launch_bounds__(1024) void k_gateup_mx(GateUpArgs a) {
     // 3. activations -> E4M3 parts and their scales in LDS
 #pragma unroll
     for (int j = 0; j < XC; ++j) {
-        const int idx = tid + j * nthreads, t = idx / tchunks, ci = idx - t * tchunks;
+        int t, ci;
+        xchunk(j, t, ci);
         uint2 hi, lo;
         const uint32_t sh = split_chunk(xv[j], &hi, &lo);
         if (t < NTOK) {
@@ -299,8 +324,15 @@ __global__ __launch_bounds__(1024) void k_gateup_mx(GateUpArgs a) {
             }
         }
     }
-    if (tid < 8) reinterpret_cast<uint32_t *>(smem + L.zero_off())[tid] = 0u;
-    lds_barrier();
+    if (kOwnX) {
+        // every wave writes the same zeros before it reads them; a wave's
+        // own LDS accesses complete in order
+        if (lane < 8) reinterpret_cast<uint32_t *>(smem + L.zero_off())[lane] = 0u;
+        wave_lds_fence();
+    } else {
+        if (tid < 8) reinterpret_cast<uint32_t *>(smem + L.zero_off())[tid] = 0u;
+        lds_barrier();
+    }
 
     // 4. the units in load order, one scaled MFMA each
     const int col = lane & 15, grp = lane >> 4;
