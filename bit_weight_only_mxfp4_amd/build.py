@@ -3,7 +3,8 @@
     python -m bit_weight_only_mxfp4_amd.build
 
 Every source is compiled for gfx950 only, without fast-math, with fp32
-denormals kept and with packed-fp32 instruction selection switched off.
+denormals kept, with packed-fp32 instruction selection switched off and with
+the leading kernel arguments preloaded into scalar registers.
 """
 from __future__ import annotations
 
@@ -24,6 +25,9 @@ ARCH = "gfx950"
 FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
          "-fno-gpu-flush-denormals-to-zero", "-fno-fast-math",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # the first 16 dwords of every kernel's arguments arrive in scalar
+         # registers at wave launch instead of through a memory load
+         "-mllvm", "-amdgpu-kernarg-preload-count=16",
          "-Wall", "-Wno-unused-function"]
 
 

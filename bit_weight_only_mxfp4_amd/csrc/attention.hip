@@ -42,6 +42,25 @@ struct AttnArgs {
     int32_t out_bf16;
 };
 
+// The argument struct with the leading kernel parameters written in: the
+// fields both kernels read before their first cache or workspace loads come
+// preloaded in scalar registers; the output pointer comes with the struct.
+__device__ __forceinline__ AttnArgs attn_hot_args(AttnArgs a, const uint16_t *q,
+                                                  const uint16_t *k, const uint16_t *v,
+                                                  float *part, float *ml, int32_t tcap, int32_t T,
+                                                  int32_t nchunks, float scale2) {
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.part = part;
+    a.ml = ml;
+    a.tcap = tcap;
+    a.T = T;
+    a.nchunks = nchunks;
+    a.scale2 = scale2;
+    return a;
+}
+
 __device__ __forceinline__ uint4 attn_load16(__amdgpu_buffer_rsrc_t r, int off) {
     const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
     return make_uint4(v.x, v.y, v.z, v.w);
@@ -77,7 +96,11 @@ __device__ __forceinline__ int attn_swz(int r) {
 // 0 through LDS, which rescales each part to the common maximum, adds them in
 // wave order and writes the normalised output -- one launch for the call.
 template <int D, int G, int NB, int W>
-__global__ __launch_bounds__(64 * W) void k_attn_partial(AttnArgs a) {
+__global__ __launch_bounds__(64 * W) void k_attn_partial(const uint16_t *q, const uint16_t *k,
+                                                        const uint16_t *v, float *part, float *ml,
+                                                        int32_t tcap, int32_t T, int32_t nchunks,
+                                                        float scale2, AttnArgs cold) {
+    const AttnArgs a = attn_hot_args(cold, q, k, v, part, ml, tcap, T, nchunks, scale2);
     static_assert(NB % 2 == 0, "blocks of 16 positions come in pairs");
     constexpr int KK = D / 32;           // score steps over d
     constexpr int CPR = D / 8;           // 16-byte chunks per V row
@@ -303,7 +326,11 @@ __device__ __forceinline__ float wave_sum(float v) { return wave_reduce<false>(v
 // Each round rescales the running sums to the new maximum.  No LDS and no
 // barrier.
 template <int D, int G>
-__global__ __launch_bounds__(64) void k_attn_combine(AttnArgs a) {
+__global__ __launch_bounds__(64) void k_attn_combine(const uint16_t *q, const uint16_t *k,
+                                                     const uint16_t *v, float *part, float *ml,
+                                                     int32_t tcap, int32_t T, int32_t nchunks,
+                                                     float scale2, AttnArgs cold) {
+    const AttnArgs a = attn_hot_args(cold, q, k, v, part, ml, tcap, T, nchunks, scale2);
     const int h = blockIdx.x, lane = threadIdx.x;
     const int g = h / G, i = h - g * G;
     const int e0 = blockIdx.y * 64 + (lane & 15) * 4, ph = lane >> 4;
@@ -363,22 +390,31 @@ int attn_chunk(int64_t d, int64_t T) {
 
 int64_t attn_chunks(int64_t d, int64_t T) { return ceil_div(T, attn_chunk(d, T)); }
 
+// Launch one attention kernel: the preloaded leading parameters, then the
+// whole struct.
+template <typename Kern>
+tt_status launch_attn(const char *what, Kern kernel, dim3 grid, dim3 block, hipStream_t s,
+                      const AttnArgs &a) {
+    return launch(what, kernel, grid, block, 0, s, a.q, a.k, a.v, a.part, a.ml, a.tcap, a.T,
+                  a.nchunks, a.scale2, a);
+}
+
 template <int D, int G>
 tt_status launch_attn(const AttnArgs &a, hipStream_t s) {
     constexpr int W = attn_single_waves<D>();
     constexpr int NB = kAttnChunk / 16;
     const bool full = attn_chunk(D, a.T) == kAttnChunk;
     if (full && a.nchunks <= W)
-        return launch("gqa attention (single workgroup)", k_attn_partial<D, G, NB, W>,
-                      dim3(1u, (unsigned)a.hkv), dim3(64 * W), 0, s, a);
+        return launch_attn("gqa attention (single workgroup)", k_attn_partial<D, G, NB, W>,
+                           dim3(1u, (unsigned)a.hkv), dim3(64 * W), s, a);
     if (full)
-        TT_TRY(launch("gqa attention (chunks)", k_attn_partial<D, G, NB, 1>,
-                      dim3((unsigned)a.nchunks, (unsigned)a.hkv), dim3(64), 0, s, a));
+        TT_TRY(launch_attn("gqa attention (chunks)", k_attn_partial<D, G, NB, 1>,
+                           dim3((unsigned)a.nchunks, (unsigned)a.hkv), dim3(64), s, a));
     else
-        TT_TRY(launch("gqa attention (chunks)", k_attn_partial<D, G, NB / 2, 1>,
-                      dim3((unsigned)a.nchunks, (unsigned)a.hkv), dim3(64), 0, s, a));
-    return launch("gqa attention (combine)", k_attn_combine<D, G>,
-                  dim3((unsigned)a.hq, (unsigned)(D / 64)), dim3(64), 0, s, a);
+        TT_TRY(launch_attn("gqa attention (chunks)", k_attn_partial<D, G, NB / 2, 1>,
+                           dim3((unsigned)a.nchunks, (unsigned)a.hkv), dim3(64), s, a));
+    return launch_attn("gqa attention (combine)", k_attn_combine<D, G>,
+                       dim3((unsigned)a.hq, (unsigned)(D / 64)), dim3(64), s, a);
 }
 
 template <int D>

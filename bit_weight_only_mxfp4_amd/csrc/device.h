@@ -186,12 +186,17 @@ __device__ __forceinline__ f32x4_t mfma_fp4_fp8(int sel, i32x8_t A, i32x8_t B, f
     }
 }
 
-// Launch a kernel whose only parameter is an argument struct and report the
-// launch's own status (not a stale error left by earlier runtime calls).
-template <typename A>
-tt_status launch(const char *what, void (*kernel)(A), dim3 grid, dim3 block, size_t lds,
-                 hipStream_t stream, const A &args) {
-    void *argv[] = {const_cast<A *>(&args)};
+// Launch a kernel and report the launch's own status (not a stale error
+// left by earlier runtime calls).  The streaming kernels take what they need
+// before their first weight load as leading scalar parameters: the library is
+// built to preload the first 16 dwords of kernel arguments into scalar
+// registers at wave launch, so those values cost no memory round trip.  The
+// rest comes in one argument struct, read after the weight loads are issued.
+template <typename T> struct same_type { using type = T; };
+template <typename... P>
+tt_status launch(const char *what, void (*kernel)(P...), dim3 grid, dim3 block, size_t lds,
+                 hipStream_t stream, const typename same_type<P>::type &...args) {
+    void *argv[] = {const_cast<void *>(static_cast<const void *>(&args))...};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, lds,
                                    stream);
     if (e != hipSuccess) return fail(TT_E_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));

@@ -74,8 +74,27 @@ __device__ __forceinline__ float f8x4_dot_bf16(uint32_t c, uint32_t xw0, uint32_
                                            as_bf16x2(xw1), acc, false);
 }
 
+// The argument struct with the leading kernel parameters written in (they
+// are preloaded into scalar registers): everything read before the weight
+// loads; the tile geometry follows from k.
+__device__ __forceinline__ F8Args f8_hot_args(F8Args a, const uint8_t *w, const void *x,
+                                              int32_t k, int32_t batch, int32_t ks) {
+    const F8Geom g = f8_geom(k);
+    a.w = w;
+    a.x = x;
+    a.k = k;
+    a.units = (int32_t)g.units;
+    a.scale_off = (int32_t)g.scale_off;
+    a.tile_stride = g.stride;
+    a.batch = batch;
+    a.ks = ks;
+    return a;
+}
+
 template <int UPW, int NT, bool XF32>
-__global__ __launch_bounds__(1024) void k_fp8_gemv(F8Args a) {
+__global__ __launch_bounds__(1024) void k_fp8_gemv(const uint8_t *w, const void *x, int32_t k,
+                                                   int32_t batch, int32_t ks_, F8Args cold) {
+    const F8Args a = f8_hot_args(cold, w, x, k, batch, ks_);
     extern __shared__ __align__(16) uint8_t smem[];
     const int ks = a.ks;
     constexpr int XSZ = XF32 ? 4 : 2;            // staged bytes per activation
@@ -209,7 +228,8 @@ tt_status launch_f8(F8Args a, hipStream_t s) {
         }
     }
     dim3 grid((unsigned)a.ntiles, (unsigned)ceil_div(a.batch, NT));
-    return launch("fp8 gemv", kern, grid, dim3(64 * a.ks), lds, s, a);
+    return launch("fp8 gemv", kern, grid, dim3(64 * a.ks), lds, s, a.w, a.x, a.k, a.batch, a.ks,
+                  a);
 }
 
 // registers a wave holds for loads in flight: its code units plus NT tokens'

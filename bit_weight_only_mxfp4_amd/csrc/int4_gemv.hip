@@ -77,9 +77,30 @@ __device__ __forceinline__ void i4_lds_barrier() {
 // pieces, then each s|z group followed by its four code units.  Units past K
 // read at an out-of-range buffer offset (zeros) and meet zero-padded
 // activations and zero piece sums, so they add exactly nothing.
+// The argument struct with the leading kernel parameters written in (they
+// are preloaded into scalar registers): everything read before the weight
+// loads; the tile geometry follows from k.
+__device__ __forceinline__ I4Args i4_hot_args(I4Args a, const uint8_t *w, const uint16_t *x,
+                                              int32_t k, int32_t batch, int32_t ks) {
+    const I4Geom g = i4_geom(k);
+    a.w = w;
+    a.x = x;
+    a.k = k;
+    a.units = (int32_t)g.units;
+    a.qv_last = (int32_t)g.qv_last;
+    a.sz_off = (int32_t)g.sz_off;
+    a.tile_stride = g.stride;
+    a.batch = batch;
+    a.ks = ks;
+    return a;
+}
+
 template <int UPW, int NT, bool XVEC>
-__global__ __launch_bounds__(1024) void k_int4_gemv(I4Args a) {
+__global__ __launch_bounds__(1024) void k_int4_gemv(const uint8_t *w, const uint16_t *x,
+                                                    int32_t k, int32_t batch, int32_t ks_,
+                                                    I4Args cold) {
     static_assert(UPW % 4 == 0 && UPW <= 16, "units per wave");
+    const I4Args a = i4_hot_args(cold, w, x, k, batch, ks_);
     extern __shared__ __align__(16) uint8_t smem[];
     const int ks = a.ks;
     const int kp = ks * UPW * 128;   // staged K per token, zero past a.k
@@ -245,8 +266,10 @@ tt_status launch_i4(I4Args a, hipStream_t s) {
     a.ks = (int32_t)ceil_div(a.units, UPW);
     dim3 grid(a.ntiles, (a.batch + NT - 1) / NT);
     const size_t lds = lds_bytes(a.ks, UPW, NT);
-    return a.xvec ? launch("int4 gemv", k_int4_gemv<UPW, NT, true>, grid, dim3(64 * a.ks), lds, s, a)
-                  : launch("int4 gemv", k_int4_gemv<UPW, NT, false>, grid, dim3(64 * a.ks), lds, s, a);
+    return a.xvec ? launch("int4 gemv", k_int4_gemv<UPW, NT, true>, grid, dim3(64 * a.ks), lds, s,
+                           a.w, a.x, a.k, a.batch, a.ks, a)
+                  : launch("int4 gemv", k_int4_gemv<UPW, NT, false>, grid, dim3(64 * a.ks), lds, s,
+                           a.w, a.x, a.k, a.batch, a.ks, a);
 }
 
 template <int UPW>

@@ -37,6 +37,14 @@
 
 #include <stdint.h>
 
+// The geometry helpers run on the host (packers, launch set-up) and in the
+// kernels (which derive a tile's offsets from its block count).
+#ifdef __HIPCC__
+#define TT_GEOM __host__ __device__ inline
+#else
+#define TT_GEOM inline
+#endif
+
 namespace tt {
 
 constexpr int kTileRows = 16;
@@ -56,7 +64,7 @@ struct MxGeom {
     int64_t stride;    // bytes per tile
 };
 
-inline MxGeom mx_geom(int64_t k) {
+TT_GEOM MxGeom mx_geom(int64_t k) {
     MxGeom g;
     g.k = k;
     g.nb = k / 32;
@@ -79,7 +87,7 @@ struct I4Geom {
     int64_t stride;
 };
 
-inline I4Geom i4_geom(int64_t k) {
+TT_GEOM I4Geom i4_geom(int64_t k) {
     I4Geom g;
     g.k = k;
     g.nq = (k + 31) / 32;
@@ -102,7 +110,7 @@ struct F8Geom {
     int64_t stride;    // bytes per tile
 };
 
-inline F8Geom f8_geom(int64_t k) {
+TT_GEOM F8Geom f8_geom(int64_t k) {
     F8Geom g;
     g.k = k;
     g.units = (k + kF8UnitK - 1) / kF8UnitK;
@@ -111,6 +119,6 @@ inline F8Geom f8_geom(int64_t k) {
     return g;
 }
 
-inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+TT_GEOM int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace tt

@@ -44,7 +44,9 @@ __device__ __forceinline__ uint32_t route_key(uint32_t bits, int e) {
 // expert's rank, and ranks 0 .. topk-1 are the selection in descending order.
 // The selected lanes publish their logits by rank; lane 0 forms the softmax
 // over them in rank order.
-__global__ __launch_bounds__(64) void k_route_topk(RouteArgs ra) {
+__global__ __launch_bounds__(64) void k_route_topk(const uint16_t *logits, int32_t n_exp_,
+                                                   int32_t topk_, int32_t *ids, float *w) {
+    const RouteArgs ra{logits, n_exp_, topk_, ids, w};
     __shared__ uint32_t keys[TT_MAX_EXPERTS];
     __shared__ float selv[TT_MAX_TOPK];
     __shared__ int32_t seli[TT_MAX_TOPK];
@@ -102,6 +104,34 @@ struct DownArgs {
     int32_t y_bf16;
 };
 
+// The argument struct with the leading kernel parameters of the down
+// kernels written in: everything read before the weight loads (the tile
+// geometry follows from the block count nb, K = inter = 32 nb; an expert's
+// pack is ceil(hidden / 16) whole tiles).
+__device__ __forceinline__ DownArgs down_hot_args(DownArgs a, const uint8_t *bank,
+                                                  const void *h, const int32_t *ids, int32_t nb,
+                                                  int32_t n_experts, int32_t hidden, int32_t topk,
+                                                  int32_t S, int32_t spr) {
+    const MxGeom g = mx_geom(32 * (int64_t)nb);
+    a.bank = bank;
+    a.h = h;
+    a.ids = ids;
+    a.nb = nb;
+    a.inter = 32 * nb;
+    a.units = (int32_t)g.units;
+    a.qv_last = (int32_t)g.qv_last;
+    a.scale_off = (int32_t)g.scale_off;
+    a.ps_off = (int32_t)g.ps_off;
+    a.tile_stride = g.stride;
+    a.n_experts = n_experts;
+    a.hidden = hidden;
+    a.expert_stride = ceil_div(hidden, kTileRows) * g.stride;
+    a.topk = topk;
+    a.S = S;
+    a.spr = spr;
+    return a;
+}
+
 // Tuning: K units (128 elements) per wave.
 #ifndef TT_DOWN_UPW
 #define TT_DOWN_UPW 8
@@ -131,7 +161,11 @@ __device__ __forceinline__ void down_lds_barrier() {
 // four code units, then the postscales.  A slot with a bad expert id gets a
 // zero-length buffer descriptor, so its loads read nothing and return zeros.
 template <int UPW>
-__global__ __launch_bounds__(1024) void k_down_combine(DownArgs a) {
+__global__ __launch_bounds__(1024) void k_down_combine(const uint8_t *bank, const void *h,
+                                                  const int32_t *ids, int32_t nb,
+                                                  int32_t n_experts, int32_t hidden, int32_t topk_,
+                                                  int32_t S_, int32_t spr_, DownArgs cold) {
+    const DownArgs a = down_hot_args(cold, bank, h, ids, nb, n_experts, hidden, topk_, S_, spr_);
     static_assert(UPW % 4 == 0 && UPW <= 16, "units per wave");
     constexpr int ESZ = 4;                       // fp32 h
     constexpr int XC = UPW * ESZ / 8;            // 16-byte chunks per thread per round
@@ -240,7 +274,11 @@ __global__ __launch_bounds__(1024) void k_down_combine(DownArgs a) {
 // 32 zero bytes (B of the unused columns), then the partial rows and the
 // postscales / weights of the combine.
 template <int UPW>
-__global__ __launch_bounds__(1024) void k_down_mx(DownArgs a) {
+__global__ __launch_bounds__(1024) void k_down_mx(const uint8_t *bank, const void *h,
+                                                  const int32_t *ids, int32_t nb,
+                                                  int32_t n_experts, int32_t hidden, int32_t topk_,
+                                                  int32_t S_, int32_t spr_, DownArgs cold) {
+    const DownArgs a = down_hot_args(cold, bank, h, ids, nb, n_experts, hidden, topk_, S_, spr_);
     static_assert(UPW % 4 == 0 && UPW <= 16, "units per wave");
     constexpr int XC = UPW / 4;                  // 16-byte chunks per thread per round
     extern __shared__ __align__(16) uint8_t smem[];
@@ -387,7 +425,8 @@ tt_status launch_down_mx(const DownArgs &a, dim3 grid, dim3 block, size_t lds, h
             raised[dev] = true;
         }
     }
-    return launch("moe down + combine (scaled MFMA)", k_down_mx<UPW>, grid, block, lds, s, a);
+    return launch("moe down + combine (scaled MFMA)", k_down_mx<UPW>, grid, block, lds, s, a.bank, a.h, a.ids, a.nb,
+                  a.n_experts, a.hidden, a.topk, a.S, a.spr, a);
 }
 
 template <int UPW>
@@ -404,7 +443,8 @@ tt_status launch_down(const DownArgs &a, dim3 grid, dim3 block, size_t lds, hipS
             raised[dev] = true;
         }
     }
-    return launch("moe down + combine", k_down_combine<UPW>, grid, block, lds, s, a);
+    return launch("moe down + combine", k_down_combine<UPW>, grid, block, lds, s, a.bank, a.h, a.ids, a.nb,
+                  a.n_experts, a.hidden, a.topk, a.S, a.spr, a);
 }
 
 }  // namespace
@@ -425,7 +465,8 @@ extern "C" tt_status tt_moe_route_topk(const void *logits, int64_t batch, int64_
     TT_TRY(check_align(w, 4, "w"));
     RouteArgs ra{static_cast<const uint16_t *>(logits), (int32_t)n_experts, (int32_t)topk, ids, w};
     tt_status st = launch("moe route top-k", k_route_topk, dim3((unsigned)batch), dim3(64), 0,
-                          static_cast<hipStream_t>(stream), ra);
+                          static_cast<hipStream_t>(stream), ra.logits, ra.n_exp, ra.topk, ra.ids,
+                          ra.w);
     if (st == TT_OK) clear_error();
     return st;
 }

@@ -48,6 +48,38 @@ struct GateUpArgs {
     float *w_out;           // fused routing: routing weights [slots]
 };
 
+// The argument struct with the leading kernel parameters of the scaled-MFMA
+// kernel written in: every field that kernel reads before its weight loads
+// comes from those parameters (preloaded), in dense and routed calls alike.
+// The tile geometry follows from the block count nb (K = 32 nb); the expert
+// stride of a bank is ntiles whole tiles; rt = topk | n_experts << 16 for
+// routed calls.
+__device__ __forceinline__ GateUpArgs gu_hot_args(GateUpArgs a, const uint8_t *w,
+                                                  const uint16_t *x, const int32_t *ids,
+                                                  const uint16_t *logits, int32_t nb,
+                                                  int32_t ntiles, int32_t ks, int32_t batch,
+                                                  int32_t rt) {
+    const MxGeom g = mx_geom(32 * (int64_t)nb);
+    a.w = w;
+    a.x = x;
+    a.ids = ids;
+    a.logits = logits;
+    a.nb = nb;
+    a.units = (int32_t)g.units;
+    a.qv_last = (int32_t)g.qv_last;
+    a.scale_off = (int32_t)g.scale_off;
+    a.ps_off = (int32_t)g.ps_off;
+    a.tile_stride = g.stride;
+    a.hidden = 32 * nb;
+    a.ntiles = ntiles;
+    a.ks = ks;
+    a.batch = batch;
+    a.topk = rt & 0xFFFF;
+    a.n_experts = rt >> 16;
+    a.expert_stride = (int64_t)ntiles * g.stride;
+    return a;
+}
+
 // Orderable key of (bf16 logit, expert index): larger logit first, then the
 // lower index; -0 folds onto +0 (the same ranking rule as the routing call).
 __device__ __forceinline__ uint32_t gu_route_key(uint32_t bits, int e) {
@@ -196,14 +228,18 @@ __host__ __device__ constexpr size_t mx_lds_bytes(int ks, int upw, int tpb) {
 // follows (FP4 codes have no NaN; the pack gives them scale byte 127) against
 // zero activations, so they add exactly zero; loads past the tile return 0.
 template <int UPW, int TPB, int NTOK>
-__global__ __launch_bounds__(1024) void k_gateup_mx(GateUpArgs a) {
+__global__ __launch_bounds__(1024) void k_gateup_mx(const uint8_t *w, const uint16_t *x,
+                                                    const int32_t *ids, const uint16_t *logits,
+                                                    int32_t nb, int32_t ntiles, int32_t ks_,
+                                                    int32_t batch, int32_t rt, GateUpArgs cold) {
     static_assert(UPW % 4 == 0 && UPW <= 16, "units per wave");
+    const GateUpArgs a = gu_hot_args(cold, w, x, ids, logits, nb, ntiles, ks_, batch, rt);
     static_assert(NTOK == 1 || NTOK == 2 || NTOK == 4 || NTOK == 8, "tokens per workgroup");
     extern __shared__ __align__(16) uint8_t smem[];
     const int ks = a.ks;
     const MxLds<NTOK> L{ks * UPW * 128};
     const int tid = threadIdx.x, lane = tid & 63;
-    const int nthreads = blockDim.x;
+    const int nthreads = 64 * TPB * a.ks;  // the launch's block size
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tsub = wave / ks, part = wave - tsub * ks;
     const int tile = blockIdx.x * TPB + tsub, slot = blockIdx.y;
@@ -241,6 +277,8 @@ __global__ __launch_bounds__(1024) void k_gateup_mx(GateUpArgs a) {
     }
 
     const uint8_t *base = a.w;
+    int route_e = 0;
+    float route_w = 0.0f;
     if (a.logits) {
         const uint16_t *lb = a.logits + (int64_t)tok0 * a.n_experts;
         uint32_t key[4];
@@ -257,10 +295,8 @@ __global__ __launch_bounds__(1024) void k_gateup_mx(GateUpArgs a) {
         const int j = slot - tok0 * a.topk;
         const bool writer = blockIdx.x == 0;
         const int e = gu_route_topj(key, a.topk, j, writer, &wj);
-        if (writer && tid == 0) {
-            a.ids_out[slot] = e;
-            a.w_out[slot] = wj;
-        }
+        route_e = e;
+        route_w = wj;
         base += (int64_t)e * a.expert_stride;
     } else if (a.ids) {
         const int e = a.ids[slot];
@@ -304,6 +340,11 @@ __global__ __launch_bounds__(1024) void k_gateup_mx(GateUpArgs a) {
     if (fin)  // uniform
         ps_own = __builtin_bit_cast(
             float, __builtin_amdgcn_raw_buffer_load_b32(rs, a.ps_off + (lane & 15) * 4, 0, 0));
+    // the routing outputs (their pointers come with the argument struct)
+    if (a.logits && blockIdx.x == 0 && tid == 0) {
+        a.ids_out[slot] = route_e;
+        a.w_out[slot] = route_w;
+    }
     // keep every load above the activation split
     __builtin_amdgcn_sched_barrier(0);
 
@@ -405,8 +446,12 @@ constexpr int kMfmaUpc = 2;    // units per K-chunk
 template <int NCOL> constexpr int mfma_slice_bytes() { return NCOL * 16 * 512; }
 
 template <int NCOL, int TMAX>
-__global__ __launch_bounds__(64 * kMfmaWaves) void k_gateup_mfma(GateUpArgs a) {
+__global__ __launch_bounds__(64 * kMfmaWaves) void k_gateup_mfma(const uint8_t *w,
+                                                                  const uint16_t *x, int32_t nb,
+                                                                  int32_t ntiles, int32_t batch,
+                                                                  int32_t blocks, GateUpArgs cold) {
     static_assert(TMAX * NCOL * 1024 <= mfma_slice_bytes<NCOL>(), "partials fit the slice");
+    const GateUpArgs a = gu_hot_args(cold, w, x, nullptr, nullptr, nb, ntiles, 1, batch, 0);
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int p = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -414,8 +459,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_gateup_mfma(GateUpArgs a) {
     const int r = lane & 15, q = lane >> 4;
     const int nkc = (a.units + kMfmaUpc - 1) / kMfmaUpc;
     // balanced split of the tiles over the workgroups: at most TMAX each
-    const int t0 = (int)((int64_t)blockIdx.x * a.ntiles / gridDim.x);
-    const int nt = (int)((int64_t)(blockIdx.x + 1) * a.ntiles / gridDim.x) - t0;
+    const int t0 = (int)((int64_t)blockIdx.x * a.ntiles / blocks);
+    const int nt = (int)((int64_t)(blockIdx.x + 1) * a.ntiles / blocks) - t0;
     const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(a.x, (int64_t)a.batch * a.hidden * 2);
 
     f32x4_t C[TMAX][NCOL];
@@ -566,7 +611,8 @@ tt_status launch_mx(const GateUpArgs &a, dim3 grid, dim3 block, size_t lds, hipS
         }
     }
     return launch("mxfp4 gate/up (scaled MFMA)", k_gateup_mx<UPW, TPB, NTOK>, grid, block, lds,
-                  stream, a);
+                  stream, a.w, a.x, a.ids, a.logits, a.nb, a.ntiles, a.ks, a.batch,
+                  a.topk | (a.n_experts << 16), a);
 }
 
 template <int UPW, int NTOK>
@@ -645,7 +691,7 @@ tt_status launch_mfma(const GateUpArgs &a, hipStream_t stream) {
     const int64_t blocks = std::max<int64_t>(
         std::min<int64_t>(a.ntiles, per_cu * device_cus()), ceil_div(a.ntiles, TMAX));
     return launch("mxfp4 gate/up (MFMA path)", k_gateup_mfma<NCOL, TMAX>, dim3((unsigned)blocks),
-                  dim3(64 * kMfmaWaves), lds, stream, a);
+                  dim3(64 * kMfmaWaves), lds, stream, a.w, a.x, a.nb, a.ntiles, a.batch, blocks, a);
 }
 
 GateUpArgs make_args(const void *w, int64_t inter, int64_t hidden, const void *x,
