@@ -8,12 +8,15 @@
 // one row; a unit is one 128-element group), all of a wave's loads in flight
 // before the activations are staged.  Decode: a code q becomes the
 // bf16 number 128 + q by OR-ing it under the exponent pattern 0x4300 (exact),
-// two at a time, and a dot2 accumulates (128 + q) * x in fp32.  Per 32-element
-// piece the activations' plain sum X is staged once, so the group term is
+// two at a time, and the bf16 matrix cores sum (128 + q) * x over each
+// 128-element group in fp32 (the tile's 16 rows are the product's columns,
+// the tokens its rows).  Per group the activations' plain sum X is staged
+// once, so the group term is
 //   s * (sum (128 + q) x - (128 + z) * X)  =  s * sum (q - z) x.
 // The activations are staged in LDS with each 8-element group reordered as
 // pairs (x0,x4) (x1,x5) (x2,x6) (x3,x7), matching the nibble pairs one
-// shift-and-mask extracts from a code dword.
+// shift-and-mask extracts from a code dword; both operands of a product
+// carry the same order, so each k slot meets its own activation.
 #include "device.h"
 #include "tt_internal.h"
 
@@ -48,19 +51,6 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t b) {
     return r;
 }
 
-__device__ __forceinline__ float i4x8_dot(uint32_t c, uint4 xg, float acc, uint32_t bias) {
-    const uint32_t m = 0x000F000Fu;
-    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(and_or(c, m, bias)), as_bf16x2(xg.x), acc,
-                                          false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(and_or(c >> 4, m, bias)), as_bf16x2(xg.y),
-                                          acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(and_or(c >> 8, m, bias)), as_bf16x2(xg.z),
-                                          acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(and_or(c >> 12, m, bias)), as_bf16x2(xg.w),
-                                          acc, false);
-    return acc;
-}
-
 __device__ __forceinline__ uint4 i4_load16(__amdgpu_buffer_rsrc_t r, int off) {
     const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
     return make_uint4(v.x, v.y, v.z, v.w);
@@ -76,7 +66,7 @@ __device__ __forceinline__ void i4_lds_barrier() {
 // [p * UPW, p * UPW + UPW).  Issue order per wave: the activations of its
 // pieces, then each s|z group followed by its four code units.  Units past K
 // read at an out-of-range buffer offset (zeros) and meet zero-padded
-// activations and zero piece sums, so they add exactly nothing.
+// activations and zero group sums, so they add exactly nothing.
 // The argument struct with the leading kernel parameters written in (they
 // are preloaded into scalar registers): everything read before the weight
 // loads; the tile geometry follows from k.
@@ -104,10 +94,10 @@ __global__ __launch_bounds__(1024) void k_int4_gemv(const uint8_t *w, const uint
     extern __shared__ __align__(16) uint8_t smem[];
     const int ks = a.ks;
     const int kp = ks * UPW * 128;   // staged K per token, zero past a.k
-    const int pieces = kp / 32;      // <= nthreads (UPW <= 16)
+    const int upk = kp / 128;        // staged units per token
     uint16_t *xs = reinterpret_cast<uint16_t *>(smem);                   // [NT][kp]
-    float *xsum = reinterpret_cast<float *>(smem + (size_t)NT * kp * 2); // [NT][pieces]
-    float *red = xsum + NT * pieces;                                     // [ks][NT][16]
+    float *xsum = reinterpret_cast<float *>(smem + (size_t)NT * kp * 2); // [NT][upk]
+    float *red = xsum + NT * upk;                                        // [ks][NT][16]
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tile = blockIdx.x, t0 = blockIdx.y * NT;
@@ -174,8 +164,9 @@ __global__ __launch_bounds__(1024) void k_int4_gemv(const uint8_t *w, const uint
     }
 
     // 3. the wave's slice to LDS: 8-element groups reordered as (x0,x4)
-    //    (x1,x5) (x2,x6) (x3,x7), and the plain sum of each 32-element piece
-    //    (the four lanes of a piece add theirs with two DPP quad swaps).  Only
+    //    (x1,x5) (x2,x6) (x3,x7), and the plain sum of each 128-element group
+    //    (the 16 lanes of a group add theirs with two DPP quad swaps and two
+    //    row rotates, in a fixed order).  Only
     //    this wave reads the slice back, and a wave's LDS accesses complete in
     //    order, so no barrier is needed.
 #pragma unroll
@@ -198,17 +189,30 @@ __global__ __launch_bounds__(1024) void k_int4_gemv(const uint8_t *w, const uint
             sum += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
                                                  0, __builtin_bit_cast(int, sum), 0x4E, 0xF, 0xF,
                                                  false));
-            if ((lane & 3) == 0) xsum[t * pieces + kw / 32 + j * 16 + (lane >> 2)] = sum;
+            // the four pieces of a unit (16 lanes): rotate by 4, then by 8
+            sum += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                 0, __builtin_bit_cast(int, sum), 0x124, 0xF, 0xF,
+                                                 false));
+            sum += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                 0, __builtin_bit_cast(int, sum), 0x128, 0xF, 0xF,
+                                                 false));
+            if ((lane & 15) == 0) xsum[t * upk + kw / 128 + j * 4 + (lane >> 4)] = sum;
         }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 
-    // 4. consume the units in load order
-    float acc[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = 0.0f;
-    const uint32_t bias = 0x43004300u;
+    // 4. each unit on the matrix cores (v_mfma_f32_16x16x32_bf16, one
+    //    product per code dword): B = the lane's own codes decoded to
+    //    128 + q (column = tile row r, k block = piece q), A = token
+    //    l % 16's activations of the same piece in the same reordered
+    //    element order (rows past NT read token NT - 1; their outputs are
+    //    never used).  C lane (row r, group g) then holds the unit's
+    //    sum of (128 + q) x for tokens 4g .. 4g+3, and the group's affine
+    //    correction is applied to it: s (C - (128 + z) sum x).
+    const int ta = min(r, NT - 1);
+    f32x4_t acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t bias = 0x43004300u, nib = 0x000F000Fu;
 #pragma unroll
     for (int i = 0; i < UPW; ++i) {
         const uint32_t sz = (i & 3) == 0 ? szv[i >> 2].x
@@ -216,40 +220,48 @@ __global__ __launch_bounds__(1024) void k_int4_gemv(const uint8_t *w, const uint
                           : (i & 3) == 2 ? szv[i >> 2].z : szv[i >> 2].w;
         const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(sz & 0xFFFFu));
         const float zb = 128.0f + (float)__builtin_bit_cast(_Float16, (uint16_t)(sz >> 16));
-        const int p = 4 * (u0 + i) + q;
+        const uint4 *xg = reinterpret_cast<const uint4 *>(xs + ta * kp + (4 * (u0 + i) + q) * 32);
+        const uint32_t cw[4] = {c[i].x, c[i].y, c[i].z, c[i].w};
+        f32x4_t cu = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const uint4 *xg = reinterpret_cast<const uint4 *>(xs + t * kp + p * 32);
-            float d0 = i4x8_dot(c[i].x, xg[0], 0.0f, bias);
-            float d1 = i4x8_dot(c[i].y, xg[1], 0.0f, bias);
-            d0 = i4x8_dot(c[i].z, xg[2], d0, bias);
-            d1 = i4x8_dot(c[i].w, xg[3], d1, bias);
-            acc[t] = fmaf(s, fmaf(-zb, xsum[t * pieces + p], d0 + d1), acc[t]);
+        for (int m = 0; m < 4; ++m) {
+            const uint4 wb = make_uint4(and_or(cw[m], nib, bias), and_or(cw[m] >> 4, nib, bias),
+                                        and_or(cw[m] >> 8, nib, bias),
+                                        and_or(cw[m] >> 12, nib, bias));
+            cu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xg[m]),
+                                                         __builtin_bit_cast(bf16x8_t, wb), cu, 0,
+                                                         0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = 4 * q + e;
+            if (t < NT)
+                acc[e] = fmaf(s, fmaf(-zb, xsum[t * upk + u0 + i], cu[e]), acc[e]);
         }
     }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        acc[t] = sum_xor32(sum_xor16(acc[t]));
-    }
     if (ks > 1) {
-        if (lane < 16)
 #pragma unroll
-            for (int t = 0; t < NT; ++t) red[(wave * NT + t) * 16 + lane] = acc[t];
+        for (int e = 0; e < 4; ++e)
+            if (4 * q + e < NT) red[(wave * NT + 4 * q + e) * 16 + r] = acc[e];
         i4_lds_barrier();
         if (wave != 0) return;
-        if (lane < 16)
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                float v = red[t * 16 + lane];
-                for (int w = 1; w < ks; ++w) v += red[(w * NT + t) * 16 + lane];
-                acc[t] = v;
+        for (int e = 0; e < 4; ++e) {
+            const int t = 4 * q + e;
+            if (t < NT) {
+                float v = red[t * 16 + r];
+                for (int w = 1; w < ks; ++w) v += red[(w * NT + t) * 16 + r];
+                acc[e] = v;
             }
+        }
     }
-    const int row = tile * 16 + lane;
-    if (lane < 16 && row < a.n)
+    const int row = tile * 16 + r;
+    if (row < a.n)
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-            if (t < nt) store_out(a.y, (int64_t)(t0 + t) * a.n + row, acc[t], a.y_bf16);
+        for (int e = 0; e < 4; ++e) {
+            const int t = 4 * q + e;
+            if (t < NT && t < nt) store_out(a.y, (int64_t)(t0 + t) * a.n + row, acc[e], a.y_bf16);
+        }
 }
 
 namespace {
@@ -258,7 +270,7 @@ constexpr size_t kLdsBudget = 64 * 1024;
 
 size_t lds_bytes(int ks, int upw, int nt) {
     const size_t kp = (size_t)ks * upw * 128;
-    return (size_t)nt * kp * 2 + (size_t)nt * (kp / 32) * 4 + (size_t)ks * nt * 64;
+    return (size_t)nt * kp * 2 + (size_t)nt * (kp / 128) * 4 + (size_t)ks * nt * 64;
 }
 
 template <int UPW, int NT>
