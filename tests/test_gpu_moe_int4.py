@@ -201,7 +201,8 @@ def _int4_case(dev, n, k, batch, layer=0, tensor=workloads.T_INT4W):
 
 @pytest.mark.parametrize("n,k,batch", [(7680, 5120, 1), (5120, 5120, 1), (100, 200, 1),
                                        (48, 328, 3), (33, 5120, 8), (16, 2, 1), (40, 130, 32),
-                                       (64, 16384, 1), (40, 16384, 3), (24, 1002, 2)])
+                                       (64, 16384, 1), (40, 16384, 3), (24, 1002, 2),
+                                       (72, 640, 5), (16, 4096, 6), (8, 256, 31)])
 def test_int4_gemv(dev, n, k, batch):
     q, s, z, packed, x = _int4_case(dev, n, k, batch)
     y = tt.int4_gemv(packed, n, k, dev_bf16(x, dev))
