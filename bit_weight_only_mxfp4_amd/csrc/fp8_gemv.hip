@@ -19,11 +19,12 @@
 // wave's own part of LDS as they are (no barrier: no other wave reads them);
 // each unit is consumed as its load lands.  fp32 activations: v_cvt_scalef32_pk_f32_fp8 (scale 1) turns two
 // E4M3 codes into two exact fp32 values, one FMA per element accumulates.
-// bf16 activations: v_cvt_scalef32_pk_bf16_fp8 turns two codes into two exact
-// bf16 values and one dot2 takes the pair (4 instead of 6 VALU ops per 4
-// codes, half the LDS reads).
-// Reduction: xor-shuffles over the 8 pieces of each row, then a fixed-order
-// cross-wave sum in LDS; the row scale multiplies the full sum.
+// Then xor-shuffles over the 8 pieces of each row.  bf16 activations:
+// v_cvt_scalef32_pk_bf16_fp8 turns two codes into two exact bf16 values and
+// the bf16 matrix cores take the products (the 8-row tile's even and odd
+// pieces as the two halves of the 16 columns, the tokens' matching pieces as
+// the rows), leaving one lane exchange per row.  A fixed-order cross-wave sum
+// in LDS follows; the row scale multiplies the full sum.
 #include "device.h"
 #include "tt_internal.h"
 
@@ -63,15 +64,11 @@ __device__ __forceinline__ float f8x4_dot(uint32_t c, float4 x, float acc) {
     return fmaf(hi.y, x.w, acc);
 }
 
-// The same against bf16 activations: v_cvt_scalef32_pk_bf16_fp8 turns two
-// codes into two exact bf16 values, and dot2 takes the pair with its two
-// activations (xw0 = x[0], x[1]; xw1 = x[2], x[3]).
-__device__ __forceinline__ float f8x4_dot_bf16(uint32_t c, uint32_t xw0, uint32_t xw1,
-                                               float acc) {
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, false),
-                                          as_bf16x2(xw0), acc, false);
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, true),
-                                           as_bf16x2(xw1), acc, false);
+// Four E4M3 codes (bytes in k order) -> four exact bf16 values, k order kept.
+__device__ __forceinline__ uint2 f8x4_to_bf16x4(uint32_t c) {
+    return make_uint2(
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, true)));
 }
 
 // The argument struct with the leading kernel parameters written in (they
@@ -152,34 +149,59 @@ __global__ __launch_bounds__(1024) void k_fp8_gemv(const uint8_t *w, const void 
     float acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = 0.0f;
+    if constexpr (XF32) {
 #pragma unroll
-    for (int i = 0; i < UPW; ++i) {
+        for (int i = 0; i < UPW; ++i) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            float d0, d1;
-            if (XF32) {
+            for (int t = 0; t < NT; ++t) {
                 const float4 *xg = reinterpret_cast<const float4 *>(xs + t * kp +
                                                                     kF8UnitK * (u0 + i) + 16 * q);
-                d0 = f8x4_dot(cu[i].x, xg[0], 0.0f);
-                d1 = f8x4_dot(cu[i].y, xg[1], 0.0f);
+                float d0 = f8x4_dot(cu[i].x, xg[0], 0.0f);
+                float d1 = f8x4_dot(cu[i].y, xg[1], 0.0f);
                 d0 = f8x4_dot(cu[i].z, xg[2], d0);
                 d1 = f8x4_dot(cu[i].w, xg[3], d1);
-            } else {
-                const uint4 *xg = reinterpret_cast<const uint4 *>(
-                    reinterpret_cast<const uint16_t *>(xs) + t * kp + kF8UnitK * (u0 + i) + 16 * q);
-                const uint4 xa = xg[0], xb = xg[1];
-                d0 = f8x4_dot_bf16(cu[i].x, xa.x, xa.y, 0.0f);
-                d1 = f8x4_dot_bf16(cu[i].y, xa.z, xa.w, 0.0f);
-                d0 = f8x4_dot_bf16(cu[i].z, xb.x, xb.y, d0);
-                d1 = f8x4_dot_bf16(cu[i].w, xb.z, xb.w, d1);
+                acc[t] += d0 + d1;
             }
-            acc[t] += d0 + d1;
         }
-    }
-    // the 8 pieces of each row -> row partial in lanes r (0..7)
+        // the 8 pieces of each row -> row partial in lanes r (0..7)
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        acc[t] = sum_xor32(sum_xor16(sum_xor8(acc[t])));
+        for (int t = 0; t < NT; ++t) acc[t] = sum_xor32(sum_xor16(sum_xor8(acc[t])));
+    } else {
+        // bf16 activations on the matrix cores (v_mfma_f32_16x16x32_bf16,
+        // two per unit: elements 0..7 and 8..15 of the lane's piece).  B =
+        // the lane's codes as exact bf16: column c = lane % 16 is tile row
+        // c % 8 with the pieces of parity c / 8, k block = lane / 16, so the
+        // lane's own piece 2 (lane / 16) + (lane / 8) % 2 sits where it was
+        // loaded.  A row i carries token i % 8's activations of the pieces of
+        // parity i / 8 (rows past the batch repeat the last token; their
+        // outputs are never used).  Rows t, columns r (< 8) then hold the
+        // even pieces' sum of tile row r for token t, rows 8 + t, columns
+        // 8 + r the odd pieces' sum: lanes r and r + 40, element t.
+        const int ri = lane & 15, kb = lane >> 4;
+        const int ta = min(ri & 7, NT - 1), par = ri >> 3;
+        static_assert(NT <= 4, "tokens of a pass fit one C element each");
+        const uint16_t *xa0 =
+            reinterpret_cast<const uint16_t *>(xs) + ta * kp + 16 * (2 * kb + par);
+        f32x4_t c0 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, c1 = c0;
+#pragma unroll
+        for (int i = 0; i < UPW; ++i) {
+            const uint4 *xg = reinterpret_cast<const uint4 *>(xa0 + kF8UnitK * (u0 + i));
+            const uint4 xlo = xg[0], xhi = xg[1];
+            const uint2 e0 = f8x4_to_bf16x4(cu[i].x), e1 = f8x4_to_bf16x4(cu[i].y);
+            const uint2 e2 = f8x4_to_bf16x4(cu[i].z), e3 = f8x4_to_bf16x4(cu[i].w);
+            const uint4 w0 = make_uint4(e0.x, e0.y, e1.x, e1.y);
+            const uint4 w1 = make_uint4(e2.x, e2.y, e3.x, e3.y);
+            c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, xlo), __builtin_bit_cast(bf16x8_t, w0), c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, xhi), __builtin_bit_cast(bf16x8_t, w1), c1, 0, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const float v = c0[t] + c1[t];
+            acc[t] = v + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                                       (lane + 40) * 4, __builtin_bit_cast(int, v)));
+        }
     }
     if (ks > 1) {
         if (lane < kF8TileRows)
