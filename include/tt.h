@@ -191,7 +191,9 @@ tt_status tt_pack_int4(const uint8_t *q, const uint16_t *s, const uint16_t *z,
  * w_gu: packed by tt_pack_mxfp4_gateup; x: bf16 [batch][hidden];
  * out: [batch][inter] of out_dtype (TT_F32 or TT_BF16, nearest-even).
  * 1 <= batch <= 32; hidden % 32 == 0, hidden <= TT_MAX_K.  Accumulation is
- * fp32.  Batch 1 runs on vector ALUs; batch > 1 on MFMA matrix cores.
+ * fp32.  Batch 1 and 2 run on the scaled FP4 x FP8 matrix instruction (each
+ * bf16 activation carried exactly as two E4M3 parts); batch 3..32 on the
+ * bf16 matrix cores.
  */
 tt_status tt_mxfp4_gateup_swiglu(const void *w_gu, int64_t inter,
                                  int64_t hidden, const void *x, int64_t batch,
@@ -260,7 +262,9 @@ tt_status tt_moe_mxfp4_down_combine(const void *down_bank, int64_t n_experts,
  * Grouped affine INT4 matvec ("numerical drift & speedups": dense INT4
  * Q/K/V/O):  y[b][r] = sum_k s[r][g(k)] * (q[r][k] - z[r][g(k)]) * x[b][k].
  * w_packed from tt_pack_int4; group must be 128; k even, k <= TT_MAX_K;
- * x bf16 [batch][k]; y [batch][n] of y_dtype.
+ * x bf16 [batch][k]; y [batch][n] of y_dtype.  Each group's sum of
+ * (128 + q) * x is taken on the bf16 matrix cores in fp32 (all operands
+ * exact in bf16), then s * (sum - (128 + z) * sum x) is added in fp32.
  */
 tt_status tt_int4_gemv(const void *w_packed, int64_t n, int64_t k,
                        int64_t group, const void *x, int64_t batch, void *y,
@@ -283,7 +287,8 @@ tt_status tt_int4_gemv(const void *w_packed, int64_t n, int64_t k,
  * tt_fp8_gemv: w_packed from tt_pack_fp8_matrix (device); x [batch][k] of
  * x_dtype (TT_F32 or TT_BF16), 16-byte aligned, k a multiple of 8 (bf16) or
  * 4 (fp32), k <= TT_MAX_K_FP8; y [batch][n] of y_dtype.  Products and sums
- * in fp32, the row scale applied to the full sum.
+ * in fp32 (bf16 activations: on the bf16 matrix cores, every operand exact),
+ * the row scale applied to the full sum.
  */
 int64_t tt_fp8_pack_bytes(int64_t n, int64_t k);
 tt_status tt_pack_fp8_matrix(const uint8_t *codes, const float *scale,
