@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "layout.h"
 #include "tt_internal.h"
 
@@ -200,6 +202,28 @@ tt_status launch(const char *what, void (*kernel)(P...), dim3 grid, dim3 block, 
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, lds,
                                    stream);
     if (e != hipSuccess) return fail(TT_E_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return TT_OK;
+}
+
+// Raise a kernel's dynamic LDS limit to the 160 KiB of a gfx950 CU, once
+// per device.  Several host threads may call this at once: the per-device
+// flags are one atomic word, and the attribute call is idempotent, so two
+// threads that both find the flag clear both make it, with the same effect.
+// Kernel is the kernel function itself (one flag word per kernel).
+constexpr int kLdsLimitBytes = 160 * 1024;
+template <auto Kernel>
+tt_status raise_lds_limit(const char *what) {
+    static std::atomic<uint64_t> raised{0};  // bit d: done on device d
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return fail(TT_E_HIP, "%s: no usable current device", what);
+    const uint64_t bit = uint64_t{1} << dev;
+    if (raised.load(std::memory_order_acquire) & bit) return TT_OK;
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(Kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kLdsLimitBytes) != hipSuccess)
+        return fail(TT_E_HIP, "%s: cannot raise the LDS limit", what);
+    raised.fetch_or(bit, std::memory_order_release);
     return TT_OK;
 }
 

@@ -237,18 +237,7 @@ tt_status launch_f8(F8Args a, hipStream_t s) {
     a.ks = (int32_t)ceil_div(a.units, UPW);
     const size_t lds = f8_lds(a.ks, UPW, NT, XF32);
     auto kern = k_fp8_gemv<UPW, NT, XF32>;
-    if (lds > 64 * 1024) {
-        static bool raised[64] = {false};
-        int dev = 0;
-        (void)hipGetDevice(&dev);
-        if (dev >= 0 && dev < 64 && !raised[dev]) {
-            if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    (int)kF8LdsMax) != hipSuccess)
-                return fail(TT_E_HIP, "cannot raise the LDS limit of the FP8 kernel");
-            raised[dev] = true;
-        }
-    }
+    if (lds > 64 * 1024) TT_TRY((raise_lds_limit<k_fp8_gemv<UPW, NT, XF32>>("fp8 gemv")));
     dim3 grid((unsigned)a.ntiles, (unsigned)ceil_div(a.batch, NT));
     return launch("fp8 gemv", kern, grid, dim3(64 * a.ks), lds, s, a.w, a.x, a.k, a.batch, a.ks,
                   a);

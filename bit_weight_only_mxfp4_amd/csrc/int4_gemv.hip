@@ -13,6 +13,10 @@
 // the tokens its rows).  Per group the activations' plain sum X is staged
 // once, so the group term is
 //   s * (sum (128 + q) x - (128 + z) * X)  =  s * sum (q - z) x.
+// The two sums are taken in different orders, so a group whose codes all
+// equal its zero point would leave a rounding residue instead of 0; the
+// packer stores a zero scale for such a group (its weights are all zero), so
+// its term is exactly 0.
 // The activations are staged in LDS with each 8-element group reordered as
 // pairs (x0,x4) (x1,x5) (x2,x6) (x3,x7), matching the nibble pairs one
 // shift-and-mask extracts from a code dword; both operands of a product
@@ -41,14 +45,12 @@ struct I4Args {
 #endif
 constexpr int kOob = 0x7FFFFF00;  // buffer offset past every tile: loads return 0
 
-// (128 + q) x summed over the 8 codes of one dword; xg holds the reordered
-// activation pairs of that 8-element group.
-// (x & m) | b in one VALU op (the compiler otherwise emits an AND and an OR:
-// VOP3 on this target reads at most one scalar, so b stays in a VGPR)
+// (x & m) | b, written in C so that the compiler sees every register it
+// writes: it must space VALU writes from the matrix instructions still in
+// flight on the same registers, and it cannot do that for inline assembly.
+// With b held in a VGPR (see k_int4_gemv) this is one v_and_or_b32.
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t b) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(b));
-    return r;
+    return (x & m) | b;
 }
 
 __device__ __forceinline__ uint4 i4_load16(__amdgpu_buffer_rsrc_t r, int off) {
@@ -212,7 +214,12 @@ __global__ __launch_bounds__(1024) void k_int4_gemv(const uint8_t *w, const uint
     //    correction is applied to it: s (C - (128 + z) sum x).
     const int ta = min(r, NT - 1);
     f32x4_t acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    const uint32_t bias = 0x43004300u, nib = 0x000F000Fu;
+    // the bias 0x4300 (bf16 128.0) in both halves, in a VGPR whose value the
+    // compiler does not fold into each use (a VOP3 op reads one scalar, and
+    // the nibble mask takes it); set once, before any matrix instruction
+    uint32_t bias;
+    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(bias));
+    const uint32_t nib = 0x000F000Fu;
 #pragma unroll
     for (int i = 0; i < UPW; ++i) {
         const uint32_t sz = (i & 3) == 0 ? szv[i >> 2].x

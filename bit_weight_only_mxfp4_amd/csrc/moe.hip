@@ -413,36 +413,14 @@ namespace {
 
 template <int UPW>
 tt_status launch_down_mx(const DownArgs &a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
-    if (lds > 64 * 1024) {
-        static bool raised[64] = {false};
-        int dev = 0;
-        (void)hipGetDevice(&dev);
-        if (dev >= 0 && dev < 64 && !raised[dev]) {
-            if (hipFuncSetAttribute(reinterpret_cast<const void *>(k_down_mx<UPW>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    160 * 1024) != hipSuccess)
-                return fail(TT_E_HIP, "cannot raise the LDS limit of the down kernel");
-            raised[dev] = true;
-        }
-    }
+    if (lds > 64 * 1024) TT_TRY((raise_lds_limit<k_down_mx<UPW>>("moe down + combine")));
     return launch("moe down + combine (scaled MFMA)", k_down_mx<UPW>, grid, block, lds, s, a.bank, a.h, a.ids, a.nb,
                   a.n_experts, a.hidden, a.topk, a.S, a.spr, a);
 }
 
 template <int UPW>
 tt_status launch_down(const DownArgs &a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
-    if (lds > 64 * 1024) {
-        static bool raised[64] = {false};
-        int dev = 0;
-        (void)hipGetDevice(&dev);
-        if (dev >= 0 && dev < 64 && !raised[dev]) {
-            if (hipFuncSetAttribute(reinterpret_cast<const void *>(k_down_combine<UPW>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    160 * 1024) != hipSuccess)
-                return fail(TT_E_HIP, "cannot raise the LDS limit of the down kernel");
-            raised[dev] = true;
-        }
-    }
+    if (lds > 64 * 1024) TT_TRY((raise_lds_limit<k_down_combine<UPW>>("moe down + combine")));
     return launch("moe down + combine", k_down_combine<UPW>, grid, block, lds, s, a.bank, a.h, a.ids, a.nb,
                   a.n_experts, a.hidden, a.topk, a.S, a.spr, a);
 }

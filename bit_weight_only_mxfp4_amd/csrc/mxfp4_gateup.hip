@@ -1,11 +1,11 @@
 // mxfp4_gateup.hip -- MXFP4 gate/up projection fused with the row postscale
 // and SwiGLU, dense and routed-expert, for gfx950.
 //
-// What is computed ("Dev Log #4", section "Where Blackwell helps": read packed
-// FP4 weights and block scales, multiply against BF16 activations, accumulate
-// safely, then apply the row postscale; "Dev Log #2": gated activation;
-// stardance page, "numerical drift & speedups": the same over the selected
-// experts):  out[r] = silu(ps_g[r] * (Wg x)[r]) * (ps_u[r] * (Wu x)[r]).
+// What is computed ("Dev Log #4", section "Where Blackwell helps": 4-bit
+// codes under block scales against bf16 activations, the row postscale on the
+// finished sum; "Dev Log #2": gated activation; stardance page, "numerical
+// drift & speedups": the same over the selected experts):
+//   out[r] = silu(ps_g[r] * (Wg x)[r]) * (ps_u[r] * (Wu x)[r]).
 //
 // Batch 1 and 2 (and the routed experts, one token per slot) run on the
 // gfx950 scaled matrix instruction: the packed FP4 tile units and their E8M0
@@ -468,7 +468,17 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_gateup_mfma(const uint8_t *
     for (int t = 0; t < TMAX; ++t)
 #pragma unroll
         for (int cb = 0; cb < NCOL; ++cb) C[t][cb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // postscales of rows 4q .. 4q+3 of tile p, which this wave finishes --
+    // every finishing wave, also one whose first K-chunk lies past K (a
+    // workgroup may own more tiles than the row has K-chunks); issued ahead
+    // of the weights, so the epilogue never waits on a load of its own
     f32x4_t ps4 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    if (p < nt) {  // uniform
+        const __amdgpu_buffer_rsrc_t rs =
+            buffer_rsrc(a.w + (int64_t)(t0 + p) * a.tile_stride, a.tile_stride);
+        ps4 = __builtin_bit_cast(
+            f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, a.ps_off + 16 * q, 0, 0));
+    }
 
     for (int kc = p; kc < nkc; kc += kMfmaWaves) {  // one round unless K > 2048
         const int u0 = kc * kMfmaUpc;
@@ -486,17 +496,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_gateup_mfma(const uint8_t *
                 xr, (__attribute__((address_space(3))) void *)(slice + i * 1024), 16,
                 (t < a.batch && k < a.hidden) ? (t * a.hidden + k) * 2 : kOob, 0, 0, 0);
         }
-        // 2. postscales of rows 4q .. 4q+3 of tile p, which this wave finishes
-        //    (issued before the weights: completion is in order, and the
-        //    epilogue must not wait on a load of its own)
-        if (kc == p) {
-            const bool ok = p < nt;
-            const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(
-                a.w + (int64_t)(ok ? t0 + p : 0) * a.tile_stride, ok ? a.tile_stride : 0);
-            ps4 = __builtin_bit_cast(
-                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, a.ps_off + 16 * q, 0, 0));
-        }
-        // 3. weights of every tile of the run: the units' scale dword, then
+        // 2. weights of every tile of the run: the units' scale dword, then
         //    the two units; tiles past the run read zeros
         uint4 c[TMAX][kMfmaUpc];
         uint32_t sd[TMAX];
@@ -515,7 +515,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_gateup_mfma(const uint8_t *
         // keep every load above this point: the scheduler would otherwise
         // sink the last ones past the first MFMAs and add a round trip
         __builtin_amdgcn_sched_barrier(0);
-        // 4. B operands from the slice: lane (r, q) takes token cb*16 + r at
+        // 3. B operands from the slice: lane (r, q) takes token cb*16 + r at
         //    elements (4u + q)*32 + 8j .. +8, i.e. piece (4u + q)*4 + j
         uint4 xb[kMfmaUpc][4][NCOL];
 #pragma unroll
@@ -528,7 +528,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_gateup_mfma(const uint8_t *
                     xb[u][j][cb] =
                         *reinterpret_cast<const uint4 *>(slice + t * 512 + ((pc + t) & 31) * 16);
                 }
-        // 5. tile by tile, each as soon as its loads land
+        // 4. tile by tile, each as soon as its loads land
 #pragma unroll
         for (int t = 0; t < TMAX; ++t) {
 #pragma unroll
@@ -547,7 +547,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_gateup_mfma(const uint8_t *
         }
     }
 
-    // 6. partial tiles into the wave's own slice (its B operands are in
+    // 5. partial tiles into the wave's own slice (its B operands are in
     //    registers by now), one barrier, fixed-order sum by the finisher
     const int nparts = min(kMfmaWaves, nkc);
     if (p < nparts) {
@@ -582,34 +582,26 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_gateup_mfma(const uint8_t *
 
 namespace {
 
+// Compute units of the current device, queried once per device (several
+// host threads may race to fill an entry; they store the same value).
 int device_cus() {
-    static int cus[64] = {0};
+    static std::atomic<int> cus[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cus[dev]) {
-        int v = 0;
+    int v = cus[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             v <= 0)
             v = 256;
-        cus[dev] = v;
+        cus[dev].store(v, std::memory_order_relaxed);
     }
-    return cus[dev];
+    return v;
 }
 
 template <int UPW, int TPB, int NTOK>
 tt_status launch_mx(const GateUpArgs &a, dim3 grid, dim3 block, size_t lds, hipStream_t stream) {
-    if (lds > 64 * 1024) {
-        static bool raised[64] = {false};
-        int dev = 0;
-        (void)hipGetDevice(&dev);
-        if (dev >= 0 && dev < 64 && !raised[dev]) {
-            if (hipFuncSetAttribute(reinterpret_cast<const void *>(k_gateup_mx<UPW, TPB, NTOK>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    (int)kMaxLdsBytes) != hipSuccess)
-                return fail(TT_E_HIP, "cannot raise the LDS limit of the gate/up kernel");
-            raised[dev] = true;
-        }
-    }
+    if (lds > 64 * 1024)
+        TT_TRY((raise_lds_limit<k_gateup_mx<UPW, TPB, NTOK>>("mxfp4 gate/up (scaled MFMA)")));
     return launch("mxfp4 gate/up (scaled MFMA)", k_gateup_mx<UPW, TPB, NTOK>, grid, block, lds,
                   stream, a.w, a.x, a.ids, a.logits, a.nb, a.ntiles, a.ks, a.batch,
                   a.topk | (a.n_experts << 16), a);
@@ -674,16 +666,8 @@ template <int NCOL>
 tt_status launch_mfma(const GateUpArgs &a, hipStream_t stream) {
     constexpr int TMAX = mfma_tmax<NCOL>();
     const size_t lds = mfma_lds(NCOL);
-    static bool attr_set[64] = {false};
-    int dev = 0;
-    (void)hipGetDevice(&dev);
-    if (lds > 64 * 1024 && dev >= 0 && dev < 64 && !attr_set[dev]) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(k_gateup_mfma<NCOL, TMAX>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)kMaxLds) != hipSuccess)
-            return fail(TT_E_HIP, "cannot raise the LDS limit of the MFMA gate/up kernel");
-        attr_set[dev] = true;
-    }
+    if (lds > 64 * 1024)
+        TT_TRY((raise_lds_limit<k_gateup_mfma<NCOL, TMAX>>("mxfp4 gate/up (MFMA path)")));
     // as many workgroups as fit the CUs at once (two with 16 tokens, one with
     // 32), never more than TMAX tiles per workgroup (the split in the kernel
     // is balanced): shorter runs put more waves on each SIMD

@@ -352,6 +352,32 @@ int64_t tt_int4_pack_bytes(int64_t n, int64_t k, int64_t group) {
     return ceil_div(n, kTileRows) * i4_geom(k).stride;
 }
 
+// The scale stored for one group.  A group whose codes all equal its zero
+// point holds only zero weights, s * (q - z) = +-0; storing a zero scale of
+// the same sign keeps every decoded weight bit for bit and makes the matvec
+// kernel's group term s * (sum (128 + q) x - (128 + z) sum x) exactly zero
+// (the two sums are rounded in different orders and would otherwise leave a
+// residue).  Non-finite scales are kept as they are.
+static uint16_t int4_pack_scale(const uint8_t *q, int64_t row, int64_t rowbytes, int64_t k0,
+                                int64_t k1, uint16_t s, uint16_t z) {
+    if ((s & 0x7C00u) == 0x7C00u) return s;
+    // z as a code: only a binary16 integer 0..15 can equal the codes
+    int zc = -1;
+    if ((z & 0x7FFFu) == 0) {
+        zc = 0;
+    } else if (!(z & 0x8000u)) {
+        const int e = (z >> 10) & 31, m = z & 1023;
+        if (e >= 15 && e <= 18 && (m & ((1 << (25 - e)) - 1)) == 0)
+            zc = (1024 + m) >> (25 - e);
+    }
+    if (zc < 0) return s;
+    for (int64_t kk = k0; kk < k1; ++kk) {
+        const uint8_t b = q[row * rowbytes + (kk >> 1)];
+        if (((kk & 1) ? (b >> 4) : (b & 15)) != zc) return s;
+    }
+    return static_cast<uint16_t>(s & 0x8000u);
+}
+
 tt_status tt_pack_int4(const uint8_t *q, const uint16_t *s, const uint16_t *z,
                        int64_t n, int64_t k, int64_t group, void *dst,
                        int64_t dst_bytes) {
@@ -390,9 +416,13 @@ tt_status tt_pack_int4(const uint8_t *q, const uint16_t *s, const uint16_t *z,
                 for (int tt_ = 0; tt_ < 4; ++tt_) {
                     int64_t row = t * kTileRows + r, gi = 4 * j + tt_;
                     uint32_t v = 0;
-                    if (row < n && gi < G)
-                        v = static_cast<uint32_t>(s[row * G + gi]) |
+                    if (row < n && gi < G) {
+                        const int64_t k0 = gi * group, k1 = k0 + group < k ? k0 + group : k;
+                        v = static_cast<uint32_t>(int4_pack_scale(q, row, rowbytes, k0, k1,
+                                                                  s[row * G + gi],
+                                                                  z[row * G + gi])) |
                             (static_cast<uint32_t>(z[row * G + gi]) << 16);
+                    }
                     memcpy(sz + kGroupBytes * j + 16 * r + 4 * tt_, &v, 4);
                 }
     }
