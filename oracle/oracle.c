@@ -18,9 +18,9 @@
  *   [DL4]  page kerbin.cskartikey.dev/@satvikhardat, "Dev Log #4 -- 91-96
  *          tok/s with Selective MXFP4", sections "Why this was not just normal
  *          quantization" (MXFP4 on gate/up, row postscale enabled) and "Where
- *          Blackwell helps" (store fewer bytes, use block scales, multiply
- *          against BF16 activations, accumulate safely, then apply the row
- *          postscale).
+ *          Blackwell helps" (the projection reads 4-bit codes under block
+ *          scales, takes bf16 activations, sums without losing precision and
+ *          multiplies each finished row sum by its postscale).
  *   [DL3]  same page, "Dev Log #3 -- SmolLM3-3B Results": the scaled FP8
  *          matvec snippet multiplies the full row sum by the row scale.
  *   [DL2]  same page, "Dev Log #2 -- Converting SafeTensors Into .thin":

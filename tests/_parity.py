@@ -69,3 +69,29 @@ def dev_u8(a, dev):
 
 def dev_bf16(bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+# ---- guard bands around device outputs ---------------------------------------
+
+GUARD = 64   # canary elements before and after an output
+_CANARY = {4: 0x7FA5A5A5, 2: 0x7FA5}
+
+
+def guarded(shape, dtype, dev):
+    """An output tensor that is a view into a larger buffer with canary bands
+    of GUARD elements on both sides (a NaN bit pattern no kernel writes).
+    Returns (view, check); check() asserts both bands are untouched."""
+    n = int(np.prod(shape))
+    buf = torch.empty(n + 2 * GUARD, dtype=dtype, device=dev)
+    isz = buf.element_size()
+    bits = buf.view(torch.int32 if isz == 4 else torch.int16)
+    bits.fill_(_CANARY[isz])
+    view = buf[GUARD:GUARD + n].view(shape)
+
+    def check():
+        torch.cuda.synchronize()
+        b = bits.cpu().numpy()
+        pat = np.array(_CANARY[isz], dtype=b.dtype)
+        assert np.all(b[:GUARD] == pat), "canary before the output was overwritten"
+        assert np.all(b[GUARD + n:] == pat), "canary after the output was overwritten"
+    return view, check

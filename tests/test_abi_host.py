@@ -154,9 +154,46 @@ def test_int4_quantizer_range_error_writes_nothing():
     assert e.value.status == -6
 
 
+def _stored_scale(q, s, z, row, g, k):
+    """The scale the packer stores for group g of a row: a zero of the same
+    sign when every code of the group equals its zero point and the scale is
+    finite, else the scale itself."""
+    codes = np.stack([q[row] & 15, q[row] >> 4], axis=1).reshape(-1)[:k]
+    grp = codes[128 * g:min(128 * (g + 1), k)].astype(np.float64)
+    sv, zv = oracle.f16_value(int(s[row, g])), oracle.f16_value(int(z[row, g]))
+    if np.isfinite(sv) and np.all(grp == zv):
+        return int(s[row, g]) & 0x8000
+    return int(s[row, g])
+
+
+def test_int4_pack_stores_zero_scale_for_zero_groups():
+    """Groups whose codes all equal the zero point get a zero scale of the
+    scale's sign; the decoded weights keep their bits."""
+    n, k = 4, 300
+    w = workloads.int4_source(2, 3, n, k)
+    w[0] = 0.0                          # quantizer: s = 1, z = 0, q = 0
+    w[1, 128:256] = 0.0
+    q, s, z = oracle.int4_quantize(w, 128)
+    q[2, 64:128] = 0x99                 # group 1 of row 2: q = z = 9, negative scale
+    z[2, 1] = oracle.f16_from_double(9.0)
+    s[2, 1] = oracle.f16_from_double(-0.5)
+    q[3, 128:150] = 0x55                # partial last group: q = z = 5
+    z[3, 2] = oracle.f16_from_double(5.0)
+    packed = tt.pack_int4(q, s, z, n, k)
+    nq = -(-k // 32)
+    sz_off = 256 * nq
+    stored = lambda r, g: int(packed[sz_off + 256 * (g // 4) + 16 * r + 4 * (g % 4):][:2]
+                              .view(np.uint16)[0])
+    for r, g, want in ((0, 0, 0), (0, 2, 0), (1, 1, 0), (2, 1, 0x8000), (3, 2, 0)):
+        assert stored(r, g) == want, (r, g, hex(stored(r, g)))
+        assert stored(r, g) == _stored_scale(q, s, z, r, g, k)
+    assert stored(1, 0) == int(s[1, 0]) != 0
+
+
 def test_int4_pack_layout():
     n, k = 20, 200
     w = workloads.int4_source(2, 0, n, k)
+    w[3, :128] = 0.0
     q, s, z = oracle.int4_quantize(w, 128)
     packed = tt.pack_int4(q, s, z, n, k)
     nq = -(-k // 32)
@@ -171,7 +208,7 @@ def test_int4_pack_layout():
             for kk in range(units):
                 v = tb[sz_off + 256 * (kk // 4) + 16 * r + 4 * (kk % 4):][:4].view(np.uint32)[0]
                 if row < n:
-                    assert v == (int(s[row, kk]) | (int(z[row, kk]) << 16))
+                    assert v == (_stored_scale(q, s, z, row, kk, k) | (int(z[row, kk]) << 16))
                 else:
                     assert v == 0
             for p in range(nq):

@@ -1,5 +1,7 @@
 """GPU parity of the routed-expert stages and the INT4 matvec against the CPU
-oracle, through the C ABI."""
+oracle, through the C ABI.  The routed-expert tests hold the gpt-oss-20b-shaped
+config's whole bank (32 experts, hidden 2880, inter 2880, top-4) on the
+device and route over all 32 logits."""
 import numpy as np
 import pytest
 import torch
@@ -7,7 +9,8 @@ import torch
 import bit_weight_only_mxfp4_amd as tt
 import oracle
 import workloads
-from _parity import (assert_parity, cosine, dev_bf16, dev_u8, gemv_tol, h_tol, to_np)
+from _parity import (assert_parity, cosine, dev_bf16, dev_u8, gemv_tol, guarded, h_tol,
+                     to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -50,29 +53,58 @@ def test_route_topk(dev, n_exp, topk, batch):
 
 @pytest.fixture(scope="module")
 def gptoss(dev):
+    """The gpt-oss-20b-shaped config's whole expert bank on the device."""
     w = workloads.GPTOSS
-    n_exp = 8   # experts held on the device for the test; ids are remapped below
-    gb = workloads.expert_bank(w, 0, "gate", n_experts=n_exp)
-    ub = workloads.expert_bank(w, 0, "up", n_experts=n_exp)
-    db = workloads.expert_bank(w, 0, "down", n_experts=n_exp)
+    n_exp = w.n_experts
+    gb = workloads.expert_bank(w, 0, "gate")
+    ub = workloads.expert_bank(w, 0, "up")
+    db = workloads.expert_bank(w, 0, "down")
     return dict(w=w, n_exp=n_exp, gb=gb, ub=ub, db=db,
                 gu=dev_u8(_bank_pack(gb, ub, n_exp, w.inter, w.hidden), dev),
                 dn=dev_u8(_down_pack(db, n_exp, w.hidden, w.inter), dev))
 
 
+def _boundary_ties(lg, topk):
+    """Plant ties where they decide the routing: the (topk+1)-th largest
+    logit of every token made equal to the topk-th (the lower expert index
+    must win the last slot), and the second largest equal to the largest."""
+    lg = lg.copy()
+    for b in range(lg.shape[0]):
+        order = np.argsort(-workloads.bf16_to_f32(lg[b]), kind="stable")
+        lg[b, order[topk]] = lg[b, order[topk - 1]]
+        lg[b, order[1]] = lg[b, order[0]]
+    return lg
+
+
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("batch", [1, 3])
 @pytest.mark.parametrize("h_dtype", [torch.float32, torch.bfloat16])
-def test_moe_layer_stages(dev, gptoss, batch, h_dtype):
+def test_moe_layer_stages(dev, gptoss, fused, batch, h_dtype):
+    """The config's layer stage by stage against the oracle: routing over 32
+    logits (separate call, or fused into the expert gate/up as the benchmark
+    runs it), expert gate/up SwiGLU, then down + combine on the device's own
+    h and routing weights.  Batch 3 carries ties at the selection boundary."""
     w, n_exp = gptoss["w"], gptoss["n_exp"]
     lg = workloads.router_logits(w.wid, 17 + batch, batch, n_exp)
+    if batch > 1:
+        lg = _boundary_ties(lg, w.topk)
     x = workloads.activations(w.wid, 0, batch, w.hidden)
-    ids, wt = tt.moe_route_topk(dev_bf16(lg, dev), w.topk)
-    h = tt.moe_mxfp4_gateup_swiglu(gptoss["gu"], n_exp, w.inter, w.hidden, dev_bf16(x, dev),
-                                   ids, out_dtype=h_dtype)
-    y = tt.moe_mxfp4_down_combine(gptoss["dn"], n_exp, w.hidden, w.inter, h, ids, wt)
+    xd, lgd = dev_bf16(x, dev), dev_bf16(lg, dev)
+    h, hcheck = guarded((batch, w.topk, w.inter), h_dtype, dev)
+    if fused:
+        _, ids, wt = tt.moe_mxfp4_route_gateup_swiglu(gptoss["gu"], n_exp, w.inter, w.hidden,
+                                                      xd, lgd, w.topk, out=h)
+    else:
+        ids, wt = tt.moe_route_topk(lgd, w.topk)
+        tt.moe_mxfp4_gateup_swiglu(gptoss["gu"], n_exp, w.inter, w.hidden, xd, ids, out=h)
+    y, ycheck = guarded((batch, w.hidden), torch.float32, dev)
+    tt.moe_mxfp4_down_combine(gptoss["dn"], n_exp, w.hidden, w.inter, h, ids, wt, out=y)
     torch.cuda.synchronize()
+    hcheck()
+    ycheck()
     rid, rw = oracle.moe_route_topk(lg, w.topk)
     assert np.array_equal(ids.cpu().numpy(), rid)
+    assert np.allclose(wt.cpu().numpy(), rw, rtol=2e-6, atol=0)
     # stage 1: expert gate/up against the oracle
     hr, Sg, Su = oracle.moe_gateup_swiglu(gptoss["gb"], gptoss["ub"], n_exp, w.inter, w.hidden,
                                           x, rid)
@@ -84,20 +116,21 @@ def test_moe_layer_stages(dev, gptoss, batch, h_dtype):
             o = oracle.mxfp4_gateup_swiglu(
                 (gptoss["gb"][0][e], gptoss["gb"][1][e], gptoss["gb"][2][e]),
                 (gptoss["ub"][0][e], gptoss["ub"][1][e], gptoss["ub"][2][e]),
-                w.inter, w.hidden, x[b])
+                w.inter, w.hidden, x[b], parallel=True)
             gr[b, j], ur[b, j] = o["g"][0], o["u"][0]
     ref = dict(h=hr, Sg=Sg, Su=Su, g=gr, u=ur)
     bf = h_dtype == torch.bfloat16
-    assert_parity(to_np(h), hr, h_tol(ref, bf16=bf), f"moe gate/up b{batch} {h_dtype}")
+    tag = f"{'fused' if fused else 'separate'} b{batch} {h_dtype}"
+    assert_parity(to_np(h), hr, h_tol(ref, bf16=bf), f"moe gate/up {tag}")
     # stage 2: down + combine on the device's own h and routing weights
     hg = to_np(h)
     yr, S = oracle.moe_down_combine(gptoss["db"], n_exp, w.hidden, w.inter, hg, rid,
                                     wt.cpu().numpy().astype(np.float64))
-    assert_parity(to_np(y), yr, gemv_tol(S, yr), f"moe down+combine b{batch} {h_dtype}")
+    assert_parity(to_np(y), yr, gemv_tol(S, yr), f"moe down+combine {tag}")
     # end to end against the all-oracle pipeline
     ye, _ = oracle.moe_down_combine(gptoss["db"], n_exp, w.hidden, w.inter, hr, rid, rw)
     c = cosine(to_np(y), ye)
-    print(f"moe end-to-end cosine b{batch} {h_dtype}: {c:.9f}")
+    print(f"moe end-to-end cosine {tag}: {c:.9f}")
     assert c >= 0.99999
 
 
@@ -105,10 +138,12 @@ def test_moe_layer_stages(dev, gptoss, batch, h_dtype):
 def test_fused_route_gateup_equals_separate_calls(dev, gptoss, batch):
     w, n_exp = gptoss["w"], gptoss["n_exp"]
     xd = dev_bf16(workloads.activations(w.wid, 2, batch, w.hidden), dev)
-    for step in range(3):
+    for step in range(4):
         lg = workloads.router_logits(w.wid, 40 + step, batch, n_exp)
         if step == 2:
             lg[:, 1::2] = lg[:, 0::2]          # planted ties
+        if step == 3:
+            lg = _boundary_ties(lg, w.topk)
         lgd = dev_bf16(lg, dev)
         ids, wt = tt.moe_route_topk(lgd, w.topk)
         h = tt.moe_mxfp4_gateup_swiglu(gptoss["gu"], n_exp, w.inter, w.hidden, xd, ids)
@@ -145,6 +180,69 @@ def test_moe_bad_ids_give_nan_rows(dev, gptoss):
     assert np.all(np.isnan(to_np(y)))
 
 
+def _nan_bank(w, which, plant):
+    """A canonical bank with E8M0 0xFF planted at (expert, row, block)."""
+    bank = workloads.expert_bank(w, 0, which)
+    scales = bank[1].copy()
+    for e, r, blk in plant:
+        scales[e, r, blk] = 0xFF
+    return bank[0], scales, bank[2]
+
+
+@pytest.mark.parametrize("h_dtype", [torch.float32, torch.bfloat16])
+def test_moe_nan_scale_blocks(dev, h_dtype):
+    """E8M0 0xFF blocks in the routed gate/up (separate and fused routing)
+    and in the down projection: NaN exactly where the oracle has it."""
+    n_exp, topk = 6, 3
+    w = workloads.Workload(9, "nanmoe", 512, 384, n_experts=n_exp, topk=topk)
+    nb_h, nb_i = w.hidden // 32, w.inter // 32
+    gb = _nan_bank(w, "gate", [(0, 3, 0), (2, 100, nb_h - 1), (5, 383, 7)])
+    ub = _nan_bank(w, "up", [(0, 7, 2), (2, 0, 0), (4, 200, nb_h - 1)])
+    db = _nan_bank(w, "down", [(1, 5, 0), (3, 511, nb_i - 1), (5, 64, 4)])
+    gu = dev_u8(_bank_pack(gb, ub, n_exp, w.inter, w.hidden), dev)
+    dn = dev_u8(_down_pack(db, n_exp, w.hidden, w.inter), dev)
+    x = workloads.activations(w.wid, 0, 2, w.hidden)
+    xd = dev_bf16(x, dev)
+    ids_np = np.array([[0, 2, 5], [4, 1, 3]], np.int32)
+    ids = torch.from_numpy(ids_np).to(dev)
+    h = tt.moe_mxfp4_gateup_swiglu(gu, n_exp, w.inter, w.hidden, xd, ids, out_dtype=h_dtype)
+    hr, Sg, Su = oracle.moe_gateup_swiglu(gb, ub, n_exp, w.inter, w.hidden, x, ids_np)
+    gr, ur = np.empty_like(hr), np.empty_like(hr)
+    for b in range(2):
+        for j in range(topk):
+            e = ids_np[b, j]
+            o = oracle.mxfp4_gateup_swiglu((gb[0][e], gb[1][e], gb[2][e]),
+                                           (ub[0][e], ub[1][e], ub[2][e]), w.inter, w.hidden, x[b])
+            gr[b, j], ur[b, j] = o["g"][0], o["u"][0]
+    assert np.isnan(hr).any()
+    ref = dict(h=hr, Sg=Sg, Su=Su, g=gr, u=ur)
+    assert_parity(to_np(h), hr, h_tol(ref, bf16=h_dtype == torch.bfloat16),
+                  f"moe gate/up NaN blocks {h_dtype}")
+    # fused routing: logits that select experts 0, 2, 5 for token 0
+    lg = np.zeros((1, n_exp), np.float32)
+    lg[0, [0, 2, 5]] = [3.0, 2.0, 1.0]
+    hf, idf, _ = tt.moe_mxfp4_route_gateup_swiglu(gu, n_exp, w.inter, w.hidden, xd[:1],
+                                                  dev_bf16(workloads.bf16_bits(lg), dev), topk,
+                                                  out_dtype=h_dtype)
+    assert np.array_equal(idf.cpu().numpy(), ids_np[:1])
+    assert_parity(to_np(hf), hr[:1], h_tol({k: v[:1] for k, v in ref.items()},
+                                           bf16=h_dtype == torch.bfloat16),
+                  f"moe fused gate/up NaN blocks {h_dtype}")
+    # down: finite h, NaN blocks in experts 1, 3 and 5
+    gen = np.random.default_rng(8)
+    hin = gen.standard_normal((2, topk, w.inter)).astype(np.float32)
+    if h_dtype == torch.bfloat16:
+        hin = workloads.bf16_to_f32(workloads.bf16_bits(hin))
+    wt = gen.uniform(0.1, 1.0, (2, topk)).astype(np.float32)
+    for dids in (np.array([[1, 0, 2], [4, 2, 0]], np.int32), ids_np):
+        y = tt.moe_mxfp4_down_combine(dn, n_exp, w.hidden, w.inter,
+                                      torch.from_numpy(hin).to(dev).to(h_dtype),
+                                      torch.from_numpy(dids).to(dev), torch.from_numpy(wt).to(dev))
+        yr, S = oracle.moe_down_combine(db, n_exp, w.hidden, w.inter, hin, dids,
+                                        wt.astype(np.float64))
+        assert_parity(to_np(y), yr, gemv_tol(S, yr), f"moe down NaN blocks {h_dtype} {dids[0]}")
+
+
 @pytest.mark.parametrize("hidden,inter,topk,h_bf16", [(96, 160, 3, False), (96, 160, 3, True),
                                                       (40, 2048, 8, True), (48, 4096, 8, False),
                                                       (33, 8192, 5, True)])
@@ -163,8 +261,10 @@ def test_moe_down_ragged(dev, hidden, inter, topk, h_bf16):
     hd = torch.from_numpy(h).to(dev)
     if h_bf16:
         hd = hd.to(torch.bfloat16)
-    y = tt.moe_mxfp4_down_combine(dn, n_exp, w.hidden, w.inter, hd,
-                                  torch.from_numpy(ids).to(dev), torch.from_numpy(wt).to(dev))
+    y, check = guarded((2, hidden), torch.float32, dev)
+    tt.moe_mxfp4_down_combine(dn, n_exp, w.hidden, w.inter, hd, torch.from_numpy(ids).to(dev),
+                              torch.from_numpy(wt).to(dev), out=y)
+    check()
     yr, S = oracle.moe_down_combine(db, n_exp, w.hidden, w.inter, h, ids, wt.astype(np.float64))
     assert_parity(to_np(y), yr, gemv_tol(S, yr), f"moe down h{hidden} i{inter} k{topk}")
 
@@ -204,17 +304,43 @@ def _int4_case(dev, n, k, batch, layer=0, tensor=workloads.T_INT4W):
                                        (64, 16384, 1), (40, 16384, 3), (24, 1002, 2),
                                        (72, 640, 5), (16, 4096, 6), (8, 256, 31)])
 def test_int4_gemv(dev, n, k, batch):
+    """Every row, including the Phi-4-shaped QKV (7680 x 5120) and O
+    (5120 x 5120) projections."""
     q, s, z, packed, x = _int4_case(dev, n, k, batch)
-    y = tt.int4_gemv(packed, n, k, dev_bf16(x, dev))
-    torch.cuda.synchronize()
-    rows = None
-    got = to_np(y)
-    if n > 2048:
-        rows = np.unique(np.concatenate([np.arange(16), np.arange(n - 16, n),
-                                         np.random.default_rng(n).choice(n, 400, replace=False)]))
-        got = got[:, rows]
-    yr, S = oracle.int4_gemv(q, s, z, n, k, 128, x, rows=rows)
-    assert_parity(got, yr, gemv_tol(S, yr), f"int4 n{n} k{k} b{batch}")
+    y, check = guarded((batch, n), torch.float32, dev)
+    tt.int4_gemv(packed, n, k, dev_bf16(x, dev), out=y)
+    check()
+    yr, S = oracle.int4_gemv(q, s, z, n, k, 128, x)
+    assert_parity(to_np(y), yr, gemv_tol(S, yr), f"int4 n{n} k{k} b{batch}")
+
+
+@pytest.mark.parametrize("batch", [1, 3, 8])
+def test_int4_zero_groups_are_exact(dev, batch):
+    """Groups whose codes all equal their zero point contribute exactly 0:
+    the quantizer's all-zero groups (s = 1, z = 0, q = 0), all-zero rows,
+    and hand-made groups with q = z = 7 under a random scale.  Rows made only
+    of such groups must come out exactly 0.0; the rest match the oracle."""
+    n, k = 64, 1000
+    wsrc = workloads.int4_source(2, 5, n, k)
+    wsrc[0] = 0.0                       # an all-zero row
+    wsrc[1, :128] = 0.0                 # all-zero first group
+    wsrc[2, 896:] = 0.0                 # all-zero partial last group (104 elements)
+    wsrc[3:6, 128:640] = 0.0            # several zero groups in the middle
+    q, s, z = oracle.int4_quantize(wsrc, 128)
+    G = -(-k // 128)
+    for r in (6, 7):                    # rows of groups with q = z = 7
+        q[r] = 0x77
+        z[r] = oracle.f16_from_double(7.0)
+        s[r] = [oracle.f16_from_double(float(v)) for v in
+                np.random.default_rng(r).uniform(1e-3, 1e-1, G)]
+    packed = dev_u8(tt.pack_int4(q, s, z, n, k), dev)
+    x = workloads.activations(2, 9, batch, k, tensor=workloads.T_OX)
+    y = to_np(tt.int4_gemv(packed, n, k, dev_bf16(x, dev)))
+    yr, S = oracle.int4_gemv(q, s, z, n, k, 128, x)
+    for r in (0, 6, 7):
+        assert np.all(yr[:, r] == 0.0)
+        assert np.all(y[:, r] == 0.0), (r, y[:, r])
+    assert_parity(y, yr, gemv_tol(S, yr), f"int4 zero groups b{batch}")
 
 
 @pytest.mark.parametrize("k", [512, 5120])

@@ -1,5 +1,7 @@
 """GPU parity of the MXFP4 gate/up SwiGLU path (dense, batch 1..32) and of the
-MXFP4 decode, against the CPU oracle, through the C ABI."""
+MXFP4 decode, against the CPU oracle, through the C ABI.  The full-size
+configs are checked on every output row (the large ones against the OpenMP
+build of the oracle, pinned bit for bit to the plain build by a CPU test)."""
 import numpy as np
 import pytest
 import torch
@@ -7,7 +9,7 @@ import torch
 import bit_weight_only_mxfp4_amd as tt
 import oracle
 import workloads
-from _parity import (assert_parity, dev_bf16, dev_u8, h_tol, to_np)
+from _parity import (REL, assert_parity, dev_bf16, dev_u8, guarded, h_tol, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -16,24 +18,23 @@ def _f32_bits(a):
     return np.ascontiguousarray(a, np.float32).view(np.uint32)
 
 
-def _sample_rows(inter, n_random, seed):
-    gen = np.random.default_rng(seed)
-    rows = set(range(min(16, inter))) | set(range(max(0, inter - 16), inter))
-    rows |= set(gen.choice(inter, size=min(n_random, inter), replace=False).tolist())
-    return np.array(sorted(rows), np.int64)
-
-
 def _gateup_case(dev, w, layer, batch, rows=None, out_dtype=torch.float32, g=None, u=None,
-                 x=None):
+                 x=None, guard=False):
     if g is None:
         g, u = workloads.gateup(w, layer)
     if x is None:
         x = workloads.activations(w.wid, layer, batch, w.hidden)
     packed = dev_u8(tt.pack_mxfp4_gateup(g, u, w.inter, w.hidden), dev)
-    h = tt.mxfp4_gateup_swiglu(packed, w.inter, w.hidden, dev_bf16(x, dev), out_dtype=out_dtype)
+    out, check = (guarded((batch, w.inter), out_dtype, dev) if guard else (None, None))
+    h = tt.mxfp4_gateup_swiglu(packed, w.inter, w.hidden, dev_bf16(x, dev), out=out,
+                               out_dtype=out_dtype)
     torch.cuda.synchronize()
+    if check:
+        check()
     got = to_np(h)
-    ref = oracle.mxfp4_gateup_swiglu(g, u, w.inter, w.hidden, x, rows=rows)
+    # large cases use the OpenMP build of the oracle (same loops, same bits)
+    big = batch * w.inter * w.hidden > 64 << 20
+    ref = oracle.mxfp4_gateup_swiglu(g, u, w.inter, w.hidden, x, rows=rows, parallel=big)
     if rows is not None:
         got = got[:, rows]
     return got, ref
@@ -101,22 +102,16 @@ def test_tiny_config_full(dev):
                                           (2880, 1024), (3200, 520), (2336, 1000), (16384, 40)])
 def test_ragged_shapes(dev, hidden, inter):
     w = workloads.Workload(9, "ragged", hidden, inter)
-    got, ref = _gateup_case(dev, w, 0, 1)
+    got, ref = _gateup_case(dev, w, 0, 1, guard=True)
     assert_parity(got, ref["h"], h_tol(ref), f"ragged h{hidden} i{inter}")
 
 
-def test_smollm3_all_layers_sampled_rows(dev):
+def test_smollm3_all_layers_every_row(dev):
+    """The SmolLM3-3B-shaped config: all 24 layers, every output row."""
     w = workloads.SMOLLM3
     for layer in range(w.layers):
-        rows = _sample_rows(w.inter, 96, layer)
-        got, ref = _gateup_case(dev, w, layer, 1, rows=rows)
-        assert_parity(got, ref["h"], h_tol(ref), f"smollm3 layer {layer} ({rows.size} rows)")
-
-
-def test_smollm3_layer0_every_row(dev):
-    w = workloads.SMOLLM3
-    got, ref = _gateup_case(dev, w, 0, 1)
-    assert_parity(got, ref["h"], h_tol(ref), "smollm3 layer 0 all rows")
+        got, ref = _gateup_case(dev, w, layer, 1)
+        assert_parity(got, ref["h"], h_tol(ref), f"smollm3 layer {layer} (all {w.inter} rows)")
 
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
@@ -129,31 +124,34 @@ def test_many_tiles_every_row(dev, out_dtype):
                   f"h5120 i9000 {out_dtype}")
 
 
-def test_phi4_gateup_sampled_rows(dev):
+def test_phi4_gateup_every_row(dev):
+    """The Phi-4-shaped gate/up (hidden 5120, inter 17920), every row."""
     w = workloads.PHI4
-    rows = _sample_rows(w.inter, 256, 1)
-    got, ref = _gateup_case(dev, w, 0, 1, rows=rows)
-    assert_parity(got, ref["h"], h_tol(ref), "phi4 gate/up")
+    got, ref = _gateup_case(dev, w, 0, 1)
+    assert_parity(got, ref["h"], h_tol(ref), f"phi4 gate/up (all {w.inter} rows)")
 
 
 @pytest.mark.parametrize("batch", [2, 4, 8, 16, 17, 32])
-def test_batched_smollm3_sampled_rows(dev, batch):
+def test_batched_smollm3_every_row(dev, batch):
+    """The batched config (SmolLM3 shapes) at each batch, every row."""
     w = workloads.BATCHED
-    rows = _sample_rows(w.inter, 64, batch)
-    got, ref = _gateup_case(dev, w, 0, batch, rows=rows)
-    assert_parity(got, ref["h"], h_tol(ref), f"batched b{batch}")
+    got, ref = _gateup_case(dev, w, 0, batch)
+    assert_parity(got, ref["h"], h_tol(ref), f"batched b{batch} (all rows)")
 
 
 # MFMA path off the SmolLM3 shape: ragged last unit (qv_last < 4), two chunks
 # per tile, a single unit, tiles past the grid (each wave walks several
-# tiles), and widths that fall back to one weight pass per token.
+# tiles), widths that fall back to one weight pass per token, and workgroups
+# that own more tiles than a row has K-chunks (the finishing waves of the
+# later tiles never enter the K loop).
 @pytest.mark.parametrize("hidden,inter,batch", [(2880, 1000, 5), (4096, 520, 9), (2336, 1000, 32),
                                                 (96, 100, 3), (32, 8, 2), (5120, 24, 4),
-                                                (2048, 20000, 32), (2048, 11008, 23)])
+                                                (2048, 20000, 32), (2048, 11008, 23),
+                                                (256, 8192, 4), (1024, 16384, 20),
+                                                (256, 16384, 32), (512, 12000, 9)])
 def test_batched_ragged_shapes(dev, hidden, inter, batch):
     w = workloads.Workload(9, "ragged", hidden, inter)
-    rows = _sample_rows(inter, 64, batch) if inter > 2048 else None
-    got, ref = _gateup_case(dev, w, 0, batch, rows=rows)
+    got, ref = _gateup_case(dev, w, 0, batch, guard=True)
     assert_parity(got, ref["h"], h_tol(ref), f"batched ragged h{hidden} i{inter} b{batch}")
 
 
@@ -275,3 +273,93 @@ def test_block_exponent_extremes(dev):
     got, ref = _gateup_case(dev, w, 0, 1, g=g, u=u, x=workloads.bf16_bits(x))
     assert np.all(np.isfinite(got))
     assert_parity(got, ref["h"], h_tol(ref), "block exponent extremes")
+
+
+# ---- E8M0 0xFF (NaN) blocks on every path ----------------------------------------
+
+@pytest.mark.parametrize("batch", [1, 2, 8, 32])
+def test_nan_scale_blocks(dev, batch):
+    """A block whose E8M0 byte is 0xFF decodes to NaN (OCP MX): every output
+    row that reads one (in its gate or its up row) is NaN, every other row
+    matches the oracle.  Covers the scaled-MFMA path (batch 1, 2) and the
+    bf16-MFMA path (batch 8, 32), with NaN blocks in the first, a middle and
+    the last block of a row, and a row whose activations over the NaN block
+    are zero (NaN times zero is still NaN)."""
+    w = workloads.Workload(9, "nanblk", 1024, 200)
+    g, u = workloads.gateup(w)
+    gs, us = g[1].copy(), u[1].copy()
+    nb = w.hidden // 32
+    for r, blk in ((0, 0), (5, nb // 2), (17, nb - 1), (40, 3), (199, 7)):
+        gs[r, blk] = 0xFF
+    for r, blk in ((9, 1), (17, 2), (120, nb - 1), (150, 0)):
+        us[r, blk] = 0xFF
+    x = workloads.activations(w.wid, 0, batch, w.hidden)
+    x[:, 3 * 32:4 * 32] = 0   # row 40's NaN block meets zero activations
+    got, ref = _gateup_case(dev, w, 0, batch, g=(g[0], gs, g[2]), u=(u[0], us, u[2]), x=x,
+                            guard=True)
+    nan_rows = {0, 5, 17, 40, 199, 9, 120, 150}
+    assert set(np.where(np.isnan(ref["h"][0]))[0].tolist()) == nan_rows
+    assert_parity(got, ref["h"], h_tol(ref), f"NaN scale blocks b{batch}")
+
+
+# ---- accumulation of the scaled FP4 x FP8 instruction, worst case --------------------
+
+def _spread_rows(inter, hidden, seed):
+    """Gate rows whose products span a wide range inside every 128-element
+    block of K (one matrix instruction adds 128 products):
+
+    rows 0..39: in each 128-block, one large product (code 6 under scale
+      byte e0) and 96 small ones of the same sign (code 0.5 under e0 - d) in
+      the other three 32-element blocks; d = r runs 0..39, so the small
+      products sit 2^-3.6 .. 2^-43 below the large one and the sweep crosses
+      whatever alignment window the instruction keeps;
+    rows 40..47: the same with the small products of the opposite sign;
+    rows 48..63: random codes under scale bytes drawn per block from
+      e0 - 40 .. e0, and random signs.
+    Up rows are 1.0 at one column under scale 127 (u = x there), so h is
+    silu(g) times that activation."""
+    gen = np.random.default_rng(seed)
+    nb = hidden // 32
+    e0 = 127
+    codes = np.zeros((inter, hidden), np.uint8)
+    scales = np.full((inter, nb), e0, np.uint8)
+    for r in range(48):
+        d = r if r < 40 else 4 + 4 * (r - 40)
+        neg = r >= 40
+        for b in range(0, nb, 4):
+            codes[r, 32 * b] = 7                               # +6 * 2^0
+            codes[r, 32 * (b + 1):32 * (b + 4)] = 9 if neg else 1   # -/+0.5
+            scales[r, b + 1:b + 4] = e0 - d
+    codes[48:] = gen.integers(0, 16, (inter - 48, hidden), dtype=np.uint8)
+    scales[48:] = gen.integers(e0 - 40, e0 + 1, (inter - 48, nb), dtype=np.uint8)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, scales, np.ones(inter, np.float32)
+
+
+@pytest.mark.parametrize("batch", [1, 2, 8])
+def test_accumulation_worst_case_k16384(dev, batch):
+    """K = 16384 with the products of every 128-element block spread over up
+    to 2^43 (see _spread_rows), activations either all 1.5 (exact in one
+    E4M3 part) or random bf16 spread over 2^-8 .. 2^8: every row within
+    2e-3 * sum |w x| of the oracle.  Batch 1 and 2 run on the scaled FP4 x
+    FP8 instruction, batch 8 on the bf16 matrix cores (for comparison).  The
+    worst err/tol is printed."""
+    hidden, inter = 16384, 64
+    w = workloads.Workload(9, "spread", hidden, inter)
+    g = _spread_rows(inter, hidden, 3)
+    uc = np.zeros((inter, hidden // 2), np.uint8)
+    uc[:, 0] = 2                                             # column 0: 1.0
+    u = (uc, np.full((inter, hidden // 32), 127, np.uint8), np.ones(inter, np.float32))
+    gen = np.random.default_rng(4)
+    x1 = np.full((batch, hidden), 1.5, np.float32)
+    mag = np.exp2(gen.uniform(-8, 8, (batch, hidden)))
+    x2 = (np.where(gen.random((batch, hidden)) < 0.5, -1.0, 1.0) * mag).astype(np.float32)
+    worst = 0.0
+    for name, xf in (("x=1.5", x1), ("x spread", x2)):
+        xf[:, 0] = 1.0                                       # u = 1 exactly
+        got, ref = _gateup_case(dev, w, 0, batch, g=g, u=u, x=workloads.bf16_bits(xf))
+        tol = h_tol(ref)
+        err = np.abs(got - ref["h"])
+        worst = max(worst, float((err / tol).max()))
+        assert_parity(got, ref["h"], tol, f"worst-case accumulation K=16384 b{batch} {name}")
+    print(f"K=16384 b{batch}: worst err/tol {worst:.3e} (REL = {REL})")
