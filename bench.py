@@ -11,8 +11,13 @@ workloads.py) and resident in HBM before timing starts.
 
 Prints one JSON line: value = effective HBM GB/s over the algorithmic bytes
 (each packed weight byte, E8M0 scale, postscale, activation and output once),
-with us_per_call, the roofline of the kernel and the CPU oracle timed on the
-host (a reported baseline, not a target).
+with us_per_call, the roofline of the kernel, the read ceiling (a plain
+16-byte-load read of the same number of bytes from the same rotating buffers,
+tt_stream_read) and the CPU oracle timed on the host (a reported baseline, not
+a target).  The default line also carries sub-records, each timed the same
+way against 8 TB/s and against its own read ceiling: the Phi-4-shaped gate/up,
+the gpt-oss-20b-shaped MoE layer (each kernel alone and the two together) and
+the Phi-4-shaped INT4 QKV and O projections (--headline-only skips them).
 
 Other workloads (--workload): tiny, phi4 (gate/up), phi4-int4 (QKV + O),
 gptoss (routing fused into the expert gate/up, then down/combine), batched
@@ -55,6 +60,27 @@ def int4_bytes(n, k, batch):
     return n * k // 2 + n * (-(-k // 128)) * 4 + batch * k * 2 + batch * n * 4
 
 
+def moe_bytes(w, h_bytes=2):
+    """Algorithmic bytes of one routed-expert layer at batch 1: (gate/up,
+    down/combine).  gate/up: topk experts' gate and up matrices, x, h;
+    down: topk experts' down matrices, h, y (ids and weights are a few
+    bytes and left out)."""
+    gu = w.topk * 2 * mx_matrix_bytes(w.inter, w.hidden) + w.hidden * 2 + w.topk * w.inter * h_bytes
+    dn = w.topk * mx_matrix_bytes(w.hidden, w.inter) + w.topk * w.inter * h_bytes + w.hidden * 4
+    return gu, dn
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def setup_gateup(tt, torch, dev, w, layers, batch, distinct=None):
     """Packed gate/up weights of `layers` layers on the device; the first
     `distinct` are generated, the rest are device copies of them."""
@@ -91,7 +117,8 @@ def profiled_traffic(kernel_sources, summary):
 
 
 def time_steps(torch, step, steps, warmup):
-    """Eager timing: `steps` back-to-back steps between two events."""
+    """`steps` back-to-back steps between two events recorded on the current
+    stream (the stream every call and graph replay here is launched on)."""
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -120,8 +147,201 @@ def capture(torch, step):
     return g
 
 
-def time_graph(torch, graph, steps, warmup):
-    return time_steps(torch, graph.replay, steps, warmup)
+def time_graph(torch, step, steps, warmup):
+    """Seconds for `steps` replays of `step` captured as one graph."""
+    return time_steps(torch, capture(torch, step).replay, steps, warmup)
+
+
+def rate(nbytes, seconds_per_call):
+    """GB/s and fraction of 8 TB/s for nbytes moved per call."""
+    gbs = nbytes / seconds_per_call / 1e9
+    return round(gbs, 2), round(gbs / PEAK_HBM_GBS, 4)
+
+
+# ---- read ceiling --------------------------------------------------------------
+
+def read_ceiling(tt, torch, bufs, nbytes, K, W, loads=4):
+    """A plain 16-byte-load read of nbytes from each of `bufs` in turn (the
+    same rotating buffers the kernel streams), captured as one graph like the
+    kernel's calls: seconds per read.  A buffer shorter than nbytes (a
+    weight pack without the call's activations and outputs) is read whole."""
+    nbytes = min([nbytes] + [b.numel() for b in bufs])
+    nbytes -= nbytes % 16
+    sink = torch.empty(1, dtype=torch.int32, device=bufs[0].device)
+
+    def step():
+        for b in bufs:
+            tt.stream_read(b, loads, sink=sink, nbytes=nbytes)
+
+    return time_graph(torch, step, K, W) / (K * len(bufs)), nbytes
+
+
+def best_read_loads(tt, torch, bufs, nbytes, K, W):
+    """Loads per lane (1, 2, 4, 8) of the fastest plain read for this size;
+    returns (loads, {loads: us per read})."""
+    sweep = {u: read_ceiling(tt, torch, bufs, nbytes, K, W, u)[0] for u in (1, 2, 4, 8)}
+    best = min(sweep, key=sweep.get)
+    return best, {str(u): round(t * 1e6, 3) for u, t in sweep.items()}
+
+
+def vs_ceiling(rec, kernel_s, ceiling):
+    """Adds the read ceiling (seconds, bytes read) to a record: the plain
+    read's time and rate, and the fraction of it the kernel reaches (ceiling
+    time over kernel time; the read covers the kernel's bytes, or its whole
+    weight buffer when that is shorter)."""
+    ceil_s, nread = ceiling
+    gbs, frac = rate(nread, ceil_s)
+    rec["read_ceiling"] = dict(us=round(ceil_s * 1e6, 3), bytes=nread, gbs=gbs,
+                               frac_of_peak=frac)
+    rec["frac_of_ceiling"] = round(ceil_s / kernel_s, 4)
+    return rec
+
+
+# ---- workloads -------------------------------------------------------------------
+
+def measure_gateup(tt, torch, dev, w, batch, K, W, distinct=None, loads=4, ceiling=True):
+    """Dense gate/up SwiGLU over `w.layers` rotating layers, one graph per
+    step.  loads = 0 sweeps the read ceiling's loads per lane on these
+    buffers and keeps the fastest.  Returns (record, per-call seconds)."""
+    layers = w.layers
+    log(f"setup {w.name}: {layers} layers ({distinct or layers} generated), batch {batch}")
+    packs, xs = setup_gateup(tt, torch, dev, w, layers, batch, distinct)
+    outs = [torch.empty((batch, w.inter), dtype=torch.float32, device=dev)
+            for _ in range(layers)]
+
+    def step():
+        for i in range(layers):
+            tt.mxfp4_gateup_swiglu(packs[i], w.inter, w.hidden, xs[i], out=outs[i])
+
+    eager = time_steps(torch, step, K, W) / (K * layers)
+    per_call = time_graph(torch, step, K, W) / (K * layers)
+    nbytes = gateup_bytes(w.inter, w.hidden, batch)
+    gbs, frac = rate(nbytes, per_call)
+    rec = dict(workload=w.name, hidden=w.hidden, inter=w.inter, batch=batch,
+               us_per_call=round(per_call * 1e6, 3), us_per_call_eager=round(eager * 1e6, 3),
+               bytes_per_call=nbytes, gbs=gbs, frac_of_peak=frac,
+               kernel="k_gateup_mx" if batch <= 2 else "k_gateup_mfma",
+               layers_rotated=layers)
+    if ceiling:
+        if not loads:
+            loads, rec["read_sweep_us"] = best_read_loads(tt, torch, packs, nbytes, K, W)
+        rec["read_loads_per_lane"] = loads
+        vs_ceiling(rec, per_call, read_ceiling(tt, torch, packs, nbytes, K, W, loads))
+    return rec, per_call
+
+
+def measure_moe(tt, torch, dev, K, W, loads=4):
+    """The gpt-oss-20b-shaped routed-expert layer at batch 1 over 24 rotating
+    layers (copies of one generated 32-expert bank, a distinct routing per
+    layer): routing fused into the expert gate/up, then down + combine; each
+    kernel alone and the whole layer, one graph per step."""
+    import workloads
+    w = workloads.GPTOSS
+    layers, E = w.layers, w.n_experts
+    log(f"setup {w.name}: 1 generated layer of {E} experts, {layers} device copies")
+    gb = workloads.expert_bank(w, 0, "gate")
+    ub = workloads.expert_bank(w, 0, "up")
+    db = workloads.expert_bank(w, 0, "down")
+    gs = tt.mxfp4_gateup_pack_bytes(w.inter, w.hidden)
+    ds = tt.mxfp4_matrix_pack_bytes(w.hidden, w.inter)
+    gu = np.empty(E * gs, np.uint8)
+    dn = np.empty(E * ds, np.uint8)
+    for e in range(E):
+        tt.pack_mxfp4_gateup((gb[0][e], gb[1][e], gb[2][e]), (ub[0][e], ub[1][e], ub[2][e]),
+                             w.inter, w.hidden, out=gu[e * gs:(e + 1) * gs])
+        tt.pack_mxfp4_matrix(db[0][e], db[1][e], db[2][e], w.hidden, w.inter,
+                             out=dn[e * ds:(e + 1) * ds])
+    del gb, ub, db
+    gu0 = torch.from_numpy(gu).to(dev)
+    dn0 = torch.from_numpy(dn).to(dev)
+    del gu, dn
+    banks = [(gu0, dn0)] + [(gu0.clone(), dn0.clone()) for _ in range(layers - 1)]
+    logits = [torch.from_numpy(workloads.router_logits(w.wid, s, 1, E).view(np.int16)).to(dev)
+              for s in range(layers)]
+    x = torch.from_numpy(workloads.activations(w.wid, 0, 1, w.hidden).view(np.int16)).to(dev)
+    ids = [torch.empty((1, w.topk), dtype=torch.int32, device=dev) for _ in range(layers)]
+    wt = [torch.empty((1, w.topk), dtype=torch.float32, device=dev) for _ in range(layers)]
+    h = [torch.empty((1, w.topk, w.inter), dtype=torch.bfloat16, device=dev)
+         for _ in range(layers)]
+    y = torch.empty((1, w.hidden), dtype=torch.float32, device=dev)
+
+    def gateup_step():
+        for li, (g_, _) in enumerate(banks):
+            tt.moe_mxfp4_route_gateup_swiglu(g_, E, w.inter, w.hidden, x, logits[li], w.topk,
+                                             ids=ids[li], w=wt[li], out=h[li])
+
+    def down_step():
+        for li, (_, d_) in enumerate(banks):
+            tt.moe_mxfp4_down_combine(d_, E, w.hidden, w.inter, h[li], ids[li], wt[li], out=y)
+
+    def layer_step():
+        for li, (g_, d_) in enumerate(banks):
+            tt.moe_mxfp4_route_gateup_swiglu(g_, E, w.inter, w.hidden, x, logits[li], w.topk,
+                                             ids=ids[li], w=wt[li], out=h[li])
+            tt.moe_mxfp4_down_combine(d_, E, w.hidden, w.inter, h[li], ids[li], wt[li], out=y)
+
+    layer_s = time_graph(torch, layer_step, K, W) / (K * layers)
+    gu_s = time_graph(torch, gateup_step, K, W) / (K * layers)   # leaves ids, w, h per layer
+    dn_s = time_graph(torch, down_step, K, W) / (K * layers)
+    gu_b, dn_b = moe_bytes(w)
+    gu_c = read_ceiling(tt, torch, [b[0] for b in banks], gu_b, K, W, loads)
+    dn_c = read_ceiling(tt, torch, [b[1] for b in banks], dn_b, K, W, loads)
+    both = gu_c[0] + dn_c[0]
+    lay_gbs, lay_frac = rate(gu_b + dn_b, layer_s)
+    rec = dict(workload=w.name, hidden=w.hidden, inter=w.inter, experts=E, topk=w.topk,
+               batch=1, h_dtype="bf16", layers_rotated=layers,
+               us_per_layer=round(layer_s * 1e6, 3), bytes_per_layer=gu_b + dn_b,
+               gbs=lay_gbs, frac_of_peak=lay_frac,
+               read_ceiling=dict(us=round(both * 1e6, 3),
+                                 note="the two reads, one launch each"),
+               frac_of_ceiling=round(both / layer_s, 4),
+               kernels={})
+    for name, kern, nb, s, c in (("gateup_routed", "k_gateup_mx (routing fused)", gu_b, gu_s,
+                                  gu_c),
+                                 ("down_combine", "k_down_mx", dn_b, dn_s, dn_c)):
+        gbs, frac = rate(nb, s)
+        rec["kernels"][name] = vs_ceiling(dict(kernel=kern, us_per_call=round(s * 1e6, 3),
+                                               bytes_per_call=nb, gbs=gbs, frac_of_peak=frac),
+                                          s, c)
+    return rec, layer_s
+
+
+def measure_int4(tt, torch, dev, K, W, loads=4):
+    """The Phi-4-shaped INT4 QKV (7680 x 5120) and O (5120 x 5120)
+    projections over 16 rotating copies, each projection timed alone."""
+    import workloads
+    w = workloads.PHI4
+    (nq, kq), (no, ko) = workloads.attention_shapes(w)
+    copies, distinct = 16, 2
+    log(f"setup INT4 QKV [{nq}x{kq}] and O [{no}x{ko}], {copies} copies")
+    packs = {"qkv": [], "o": []}
+    for layer in range(distinct):
+        for name, (n, k, tid) in (("qkv", (nq, kq, workloads.T_INT4W)),
+                                  ("o", (no, ko, workloads.T_INT4W + 100))):
+            q, s, z = tt.quantize_int4_affine(workloads.int4_source(w.wid, layer, n, k, tid))
+            packs[name].append(torch.from_numpy(tt.pack_int4(q, s, z, n, k)).to(dev))
+    for name in packs:
+        while len(packs[name]) < copies:
+            packs[name].append(packs[name][len(packs[name]) % distinct].clone())
+    x = torch.from_numpy(workloads.activations(w.wid, 0, 1, kq, workloads.T_OX)
+                         .view(np.int16)).to(dev)
+    rec = {}
+    for name, (n, k) in (("qkv", (nq, kq)), ("o", (no, ko))):
+        y = torch.empty((1, n), dtype=torch.float32, device=dev)
+        ps = packs[name]
+
+        def step(ps=ps, n=n, k=k, y=y):
+            for p in ps:
+                tt.int4_gemv(p, n, k, x, out=y)
+
+        s = time_graph(torch, step, K, W) / (K * copies)
+        nb = int4_bytes(n, k, 1)
+        gbs, frac = rate(nb, s)
+        rec[name] = vs_ceiling(dict(shape=[n, k], group=128, kernel="k_int4_gemv",
+                                    us_per_call=round(s * 1e6, 3), bytes_per_call=nb, gbs=gbs,
+                                    frac_of_peak=frac),
+                               s, read_ceiling(tt, torch, ps, nb, K, W, loads))
+    return rec
 
 
 def cpu_baseline_gateup(w, seconds):
@@ -149,7 +369,7 @@ def cpu_baseline_gateup(w, seconds):
     tp, cp, bp = timed(True, seconds / 3)
     nthr = oracle.threads(parallel=True)
     return dict(value=round(nbytes / t_total / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
-                us_per_call=round(t_total / calls * 1e6, 1),
+                cpu_model=cpu_model(), us_per_call=round(t_total / calls * 1e6, 1),
                 sample=f"{calls} full {w.name} layer calls (batch 1), single thread, "
                        f"fp64 oracle, {t_total:.1f} s",
                 parallel=dict(value=round(bp / tp / 1e9, 4), unit="GB/s", cores=nthr,
@@ -157,6 +377,9 @@ def cpu_baseline_gateup(w, seconds):
                               sample=f"{cp} full {w.name} layer calls, the same oracle loops "
                                      f"with rows split over {nthr} OpenMP threads, "
                                      f"{tp:.1f} s"))
+
+
+GATEUP_METRIC = "effective HBM GB/s of the MXFP4 gate/up SwiGLU GEMV (us/call alongside)"
 
 
 def run(args):
@@ -174,138 +397,88 @@ def run(args):
         w = {"smollm3": workloads.SMOLLM3, "tiny": workloads.TINY, "phi4": workloads.PHI4,
              "batched": workloads.BATCHED}[args.workload]
         batch = args.batch if args.workload == "batched" else 1
-        layers = w.layers
-        distinct = min(layers, 4) if args.workload == "phi4" else layers
-        log(f"setup {w.name}: {layers} layers, batch {batch}")
-        packs, xs = setup_gateup(tt, torch, dev, w, layers, batch, distinct)
-        outs = [torch.empty((batch, w.inter), dtype=torch.float32, device=dev)
-                for _ in range(layers)]
-
-        def step():
-            for i in range(layers):
-                tt.mxfp4_gateup_swiglu(packs[i], w.inter, w.hidden, xs[i], out=outs[i])
-
-        eager = time_steps(torch, step, K, W)
-        secs = time_graph(torch, capture(torch, step), K, W)
-        calls = K * layers
-        per_call = gateup_bytes(w.inter, w.hidden, batch)
-        us_call = secs / calls * 1e6
-        gbs = per_call * calls / secs / 1e9
-        kernel = "k_gateup_mx" if batch <= 2 else "k_gateup_mfma"
-        result = dict(metric="effective HBM GB/s of the MXFP4 gate/up SwiGLU GEMV "
-                             "(us/call alongside)",
-                      value=round(gbs, 2), unit="GB/s", us_per_call=round(us_call, 3),
-                      us_per_call_eager=round(eager / calls * 1e6, 3),
-                      ms_per_step=round(secs / K * 1e3, 4), bytes_per_call=per_call,
+        distinct = min(w.layers, 4) if args.workload == "phi4" else None
+        # the read ceiling's loads per lane: swept on the headline's buffers
+        # (the fastest plain read of its bytes), then used for every ceiling
+        rec, per_call = measure_gateup(tt, torch, dev, w, batch, K, W, distinct,
+                                       args.read_loads, ceiling=args.workload != "tiny")
+        loads = rec.get("read_loads_per_lane", 4)
+        calls = K * w.layers
+        result = dict(metric=GATEUP_METRIC, value=rec["gbs"], unit="GB/s",
+                      us_per_call=rec["us_per_call"], us_per_call_eager=rec["us_per_call_eager"],
+                      ms_per_step=round(per_call * w.layers * 1e3, 4),
+                      bytes_per_call=rec["bytes_per_call"],
                       config=dict(workload=w.name, hidden=w.hidden, inter=w.inter, batch=batch,
-                                  layers_rotated=layers, calls_per_step=layers,
+                                  layers_rotated=w.layers, calls_per_step=w.layers,
                                   launch="one HIP graph per step"),
-                      roofline=dict(bound="hbm", kernel=kernel, achieved=round(gbs, 2),
-                                    peak=PEAK_HBM_GBS, unit="GB/s",
-                                    frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
+                      roofline=dict(bound="hbm", kernel=rec["kernel"], achieved=rec["gbs"],
+                                    peak=PEAK_HBM_GBS, unit="GB/s", frac=rec["frac_of_peak"],
+                                    traffic=None,
+                                    basis=f"algorithmic bytes per call / average per-call time "
+                                          f"of {calls} graph-replayed calls (HIP events)"))
+        if "read_ceiling" in rec:
+            result["read_ceiling"] = dict(rec["read_ceiling"], kernel="k_stream_read",
+                                          loads_per_lane=loads,
+                                          sweep_us=rec.get("read_sweep_us"))
+            result["frac_of_ceiling"] = rec["frac_of_ceiling"]
         if args.workload == "smollm3":
             result["roofline"]["traffic"] = profiled_traffic(
                 ("mxfp4_gateup.hip", "device.h", "layout.h"), "gateup_smollm3_b1.md")
+            if not args.headline_only:
+                log("sub-records ...")
+                sub = {}
+                phi, _ = measure_gateup(tt, torch, dev, workloads.PHI4, 1, K, W, 4, loads)
+                sub["phi4_gateup"] = phi
+                torch.cuda.empty_cache()
+                sub["gptoss_moe_layer"], _ = measure_moe(tt, torch, dev, K, W, loads)
+                torch.cuda.empty_cache()
+                sub["phi4_int4"] = measure_int4(tt, torch, dev, K, W, loads)
+                torch.cuda.empty_cache()
+                result["subrecords"] = sub
         if not args.no_cpu_baseline and args.workload in ("smollm3", "tiny"):
             log("cpu baseline (oracle) ...")
             result["cpu_baseline"] = cpu_baseline_gateup(w, args.cpu_seconds)
 
     elif args.workload == "phi4-int4":
-        w = workloads.PHI4
-        (nq, kq), (no, ko) = workloads.attention_shapes(w)
-        copies, distinct = 16, 2
-        log(f"setup INT4 QKV [{nq}x{kq}] and O [{no}x{ko}], {copies} copies")
-        packs = []
-        for layer in range(distinct):
-            pr = []
-            for (n, k, tid) in ((nq, kq, workloads.T_INT4W), (no, ko, workloads.T_INT4W + 100)):
-                q, s, z = tt.quantize_int4_affine(workloads.int4_source(w.wid, layer, n, k, tid))
-                pr.append(torch.from_numpy(tt.pack_int4(q, s, z, n, k)).to(dev))
-            packs.append(pr)
-        while len(packs) < copies:
-            packs.append([p.clone() for p in packs[len(packs) % distinct]])
-        x = torch.from_numpy(workloads.activations(w.wid, 0, 1, kq, workloads.T_OX)
-                             .view(np.int16)).to(dev)
-        yq = torch.empty((1, nq), dtype=torch.float32, device=dev)
-        yo = torch.empty((1, no), dtype=torch.float32, device=dev)
-
-        def step():
-            for pq, po in packs:
-                tt.int4_gemv(pq, nq, kq, x, out=yq)
-                tt.int4_gemv(po, no, ko, x, out=yo)
-
-        secs = time_graph(torch, capture(torch, step), K, W)
-        per_pair = int4_bytes(nq, kq, 1) + int4_bytes(no, ko, 1)
-        calls = K * copies * 2
-        gbs = per_pair * copies * K / secs / 1e9
+        rec = measure_int4(tt, torch, dev, K, W, args.read_loads or 4)
+        q, o = rec["qkv"], rec["o"]
+        per_pair = q["bytes_per_call"] + o["bytes_per_call"]
+        secs = (q["us_per_call"] + o["us_per_call"]) * 1e-6
+        gbs, frac = rate(per_pair, secs)
         result = dict(metric="effective HBM GB/s of the grouped affine INT4 GEMV (QKV + O)",
-                      value=round(gbs, 2), unit="GB/s", us_per_call=round(secs / calls * 1e6, 3),
-                      ms_per_step=round(secs / K * 1e3, 4),
-                      config=dict(workload="phi4-14b-int4-qkv-o", qkv=[nq, kq], o=[no, ko],
-                                  group=128, copies_rotated=copies,
-                                  launch="one HIP graph per step"),
-                      roofline=dict(bound="hbm", kernel="k_int4_gemv", achieved=round(gbs, 2),
-                                    peak=PEAK_HBM_GBS, unit="GB/s",
-                                    frac=round(gbs / PEAK_HBM_GBS, 4),
+                      value=gbs, unit="GB/s", us_per_call=round(secs / 2 * 1e6, 3),
+                      ms_per_step=round(secs * 16 * 1e3, 4),
+                      config=dict(workload="phi4-14b-int4-qkv-o", qkv=q["shape"], o=o["shape"],
+                                  group=128, copies_rotated=16,
+                                  launch="one HIP graph per projection and step"),
+                      roofline=dict(bound="hbm", kernel="k_int4_gemv", achieved=gbs,
+                                    peak=PEAK_HBM_GBS, unit="GB/s", frac=frac,
                                     traffic=profiled_traffic(
                                         ("int4_gemv.hip", "device.h", "layout.h"),
-                                        "int4_phi4_qkv_o.md")))
+                                        "int4_phi4_qkv_o.md")),
+                      projections=rec)
 
     elif args.workload == "gptoss":
-        w = workloads.GPTOSS
-        layers, E = w.layers, w.n_experts
-        log(f"setup {w.name}: 1 generated layer of {E} experts, {layers} device copies")
-        gb = workloads.expert_bank(w, 0, "gate")
-        ub = workloads.expert_bank(w, 0, "up")
-        db = workloads.expert_bank(w, 0, "down")
-        gs = tt.mxfp4_gateup_pack_bytes(w.inter, w.hidden)
-        ds = tt.mxfp4_matrix_pack_bytes(w.hidden, w.inter)
-        gu = np.empty(E * gs, np.uint8)
-        dn = np.empty(E * ds, np.uint8)
-        for e in range(E):
-            tt.pack_mxfp4_gateup((gb[0][e], gb[1][e], gb[2][e]), (ub[0][e], ub[1][e], ub[2][e]),
-                                 w.inter, w.hidden, out=gu[e * gs:(e + 1) * gs])
-            tt.pack_mxfp4_matrix(db[0][e], db[1][e], db[2][e], w.hidden, w.inter,
-                                 out=dn[e * ds:(e + 1) * ds])
-        del gb, ub, db
-        gu0 = torch.from_numpy(gu).to(dev)
-        dn0 = torch.from_numpy(dn).to(dev)
-        banks = [(gu0, dn0)] + [(gu0.clone(), dn0.clone()) for _ in range(layers - 1)]
-        logits = [torch.from_numpy(workloads.router_logits(w.wid, s, 1, E).view(np.int16)).to(dev)
-                  for s in range(layers)]
-        x = torch.from_numpy(workloads.activations(w.wid, 0, 1, w.hidden).view(np.int16)).to(dev)
-        ids = torch.empty((1, w.topk), dtype=torch.int32, device=dev)
-        wt = torch.empty((1, w.topk), dtype=torch.float32, device=dev)
-        h = torch.empty((1, w.topk, w.inter), dtype=torch.bfloat16, device=dev)
-        y = torch.empty((1, w.hidden), dtype=torch.float32, device=dev)
-        def step():
-            # routing fused into the expert gate/up call, then down + combine
-            for li, (g_, d_) in enumerate(banks):
-                tt.moe_mxfp4_route_gateup_swiglu(g_, E, w.inter, w.hidden, x, logits[li], w.topk,
-                                                 ids=ids, w=wt, out=h)
-                tt.moe_mxfp4_down_combine(d_, E, w.hidden, w.inter, h, ids, wt, out=y)
-
-        secs = time_graph(torch, capture(torch, step), K, W)
-        per_layer = (w.topk * (2 * mx_matrix_bytes(w.inter, w.hidden)) + w.hidden * 2
-                     + w.topk * w.inter * 2) + (w.topk * mx_matrix_bytes(w.hidden, w.inter)
-                                                + w.topk * w.inter * 2 + w.hidden * 4)
-        gbs = per_layer * layers * K / secs / 1e9
+        rec, layer_s = measure_moe(tt, torch, dev, K, W, args.read_loads or 4)
         result = dict(metric="effective HBM GB/s of the routed-expert MXFP4 layer "
                              "(route + expert gate/up SwiGLU + down/combine)",
-                      value=round(gbs, 2), unit="GB/s",
-                      us_per_layer=round(secs / (K * layers) * 1e6, 3),
-                      ms_per_step=round(secs / K * 1e3, 4),
-                      config=dict(workload=w.name, hidden=w.hidden, inter=w.inter, experts=E,
-                                  topk=w.topk, batch=1, layers_rotated=layers, h_dtype="bf16",
+                      value=rec["gbs"], unit="GB/s", us_per_layer=rec["us_per_layer"],
+                      ms_per_step=round(layer_s * rec["layers_rotated"] * 1e3, 4),
+                      config=dict(workload=rec["workload"], hidden=rec["hidden"],
+                                  inter=rec["inter"], experts=rec["experts"], topk=rec["topk"],
+                                  batch=1, layers_rotated=rec["layers_rotated"], h_dtype="bf16",
                                   routing="a distinct seeded routing per layer, fused into "
                                           "the expert gate/up call",
                                   launch="one HIP graph per step"),
                       roofline=dict(bound="hbm", kernel="k_gateup_mx(routed)+k_down_mx",
-                                    achieved=round(gbs, 2), peak=PEAK_HBM_GBS, unit="GB/s",
-                                    frac=round(gbs / PEAK_HBM_GBS, 4),
+                                    achieved=rec["gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
+                                    frac=rec["frac_of_peak"],
                                     traffic=profiled_traffic(
                                         ("mxfp4_gateup.hip", "moe.hip", "device.h", "layout.h"),
-                                        "moe_gptoss_layer.md")))
+                                        "moe_gptoss_layer.md")),
+                      kernels=rec["kernels"], read_ceiling=rec["read_ceiling"],
+                      frac_of_ceiling=rec["frac_of_ceiling"])
+
     elif args.workload == "fp8-down":
         # the dense down projection of the SmolLM3-shaped MLP as a row-scaled
         # FP8 matvec on the gate/up SwiGLU output h (fp32), batch 1
@@ -324,22 +497,23 @@ def run(args):
             for p in packs:
                 tt.fp8_gemv(p, n, k, h, out=y)
 
-        secs = time_graph(torch, capture(torch, step), K, W)
+        secs = time_graph(torch, step, K, W)
         calls = K * layers
         per_call = n * k + n * 4 + k * 4 + n * 4
-        gbs = per_call * calls / secs / 1e9
+        gbs, frac = rate(per_call, secs / calls)
         result = dict(metric="effective HBM GB/s of the row-scaled FP8 E4M3 down projection",
-                      value=round(gbs, 2), unit="GB/s", us_per_call=round(secs / calls * 1e6, 3),
+                      value=gbs, unit="GB/s", us_per_call=round(secs / calls * 1e6, 3),
                       ms_per_step=round(secs / K * 1e3, 4), bytes_per_call=per_call,
                       config=dict(workload="smollm3-3b-fp8-down-h2048-i11008", n=n, k=k,
                                   batch=1, x="fp32 SwiGLU output", layers_rotated=layers,
                                   launch="one HIP graph per step"),
-                      roofline=dict(bound="hbm", kernel="k_fp8_gemv", achieved=round(gbs, 2),
-                                    peak=PEAK_HBM_GBS, unit="GB/s",
-                                    frac=round(gbs / PEAK_HBM_GBS, 4),
+                      roofline=dict(bound="hbm", kernel="k_fp8_gemv", achieved=gbs,
+                                    peak=PEAK_HBM_GBS, unit="GB/s", frac=frac,
                                     traffic=profiled_traffic(
                                         ("fp8_gemv.hip", "device.h", "layout.h"),
                                         "fp8_down_smollm3.md")))
+        vs_ceiling(result, secs / calls,
+                   read_ceiling(tt, torch, packs, per_call, K, W, args.read_loads or 4))
 
     elif args.workload == "attention":
         # single-token GQA attention, Phi-4-shaped heads by default (40 query /
@@ -368,13 +542,13 @@ def run(args):
             for kc_, vc_ in caches:
                 tt.gqa_attention_decode(q, kc_, vc_, hq, hkv, d, T, scale, out=out, workspace=ws)
 
-        secs = time_graph(torch, capture(torch, step), K, W)
+        secs = time_graph(torch, step, K, W)
         calls = K * layers
         per_call = 2 * hkv * T * d * 2 + hq * d * 2 + hq * d * 4
-        gbs = per_call * calls / secs / 1e9
+        gbs, frac = rate(per_call, secs / calls)
         result = dict(metric="effective HBM GB/s of single-token GQA attention over a bf16 KV "
                              "cache",
-                      value=round(gbs, 2), unit="GB/s", us_per_call=round(secs / calls * 1e6, 3),
+                      value=gbs, unit="GB/s", us_per_call=round(secs / calls * 1e6, 3),
                       ms_per_step=round(secs / K * 1e3, 4), bytes_per_call=per_call,
                       config=dict(workload=(f"phi4-14b-gqa-attention-40-10x128-T{T}"
                                             if (hq, hkv, d) == (40, 10, 128) else
@@ -382,8 +556,7 @@ def run(args):
                                   hkv=hkv, d=d, T=T, layers_rotated=layers,
                                   launch="one HIP graph per step (2 kernels per call)"),
                       roofline=dict(bound="hbm", kernel="k_attn_partial+k_attn_combine",
-                                    achieved=round(gbs, 2), peak=PEAK_HBM_GBS, unit="GB/s",
-                                    frac=round(gbs / PEAK_HBM_GBS, 4),
+                                    achieved=gbs, peak=PEAK_HBM_GBS, unit="GB/s", frac=frac,
                                     traffic=profiled_traffic(
                                         ("attention.hip", "device.h"),
                                         "attention_phi4_t4096.md")
@@ -442,18 +615,17 @@ def run(args):
         per_layer = (int4_bytes(nq, kq, 1) - nq * 2 + 2 * hkv * T * d * 2 + hq * d * 2
                      + int4_bytes(no, ko, 1) - no * 2 + gateup_bytes(w.inter, w.hidden, 1, 2)
                      + w.hidden * w.inter + w.hidden * 4 + w.inter * 2 + w.hidden * 4)
-        gbs = per_layer * layers * K / secs / 1e9
+        gbs, frac = rate(per_layer, secs / (K * layers))
         result = dict(metric="effective HBM GB/s of one dense decode layer run as one HIP graph "
                              "(INT4 QKV, GQA attention, INT4 O, MXFP4 gate/up SwiGLU, FP8 down)",
-                      value=round(gbs, 2), unit="GB/s",
+                      value=gbs, unit="GB/s",
                       us_per_layer=round(secs / (K * layers) * 1e6, 3),
                       ms_per_step=round(secs / K * 1e3, 4), bytes_per_layer=per_layer,
                       config=dict(workload=f"phi4-14b-decode-layer-T{T}", hidden=w.hidden,
                                   inter=w.inter, heads=[hq, hkv, d], T=T, layers_rotated=layers,
                                   launch="one HIP graph per layer (6 kernels)"),
-                      roofline=dict(bound="hbm", kernel="layer graph", achieved=round(gbs, 2),
-                                    peak=PEAK_HBM_GBS, unit="GB/s",
-                                    frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None))
+                      roofline=dict(bound="hbm", kernel="layer graph", achieved=gbs,
+                                    peak=PEAK_HBM_GBS, unit="GB/s", frac=frac, traffic=None))
 
     elif args.workload == "quantize":
         # host-side MXFP4 quantizer + postscale fit on one SmolLM3-shaped
@@ -482,17 +654,17 @@ def run(args):
             oracle.mxfp4_quantize(wu)
             osecs = time.perf_counter() - t0
             result["cpu_baseline"] = dict(value=round(nbytes / osecs / 1e9, 3), unit="GB/s",
-                                          cores=1, kind="oracle",
+                                          cores=1, kind="oracle", cpu_model=cpu_model(),
                                           sample="one layer's gate and up rows, single thread")
     else:
         raise SystemExit(f"unknown workload {args.workload}")
 
+    scaled = "fp4-e2m1 x bf16 (as two e4m3 parts) on the scaled matrix instruction"
     dtype = {"phi4-int4": "int4 x bf16 -> fp32 accumulate",
              "phi4-layer": "int4 / fp4-e2m1 / fp8-e4m3 / bf16 x bf16 -> fp32 accumulate",
              "attention": "bf16 x bf16 -> fp32 accumulate",
              "fp8-down": "fp8-e4m3 x fp32 -> fp32 accumulate",
-             "quantize": "fp32 -> fp4-e2m1 + e8m0 (host)"}.get(
-                 args.workload, "fp4-e2m1 x bf16 (two e4m3 parts) -> fp32 accumulate")
+             "quantize": "fp32 -> fp4-e2m1 + e8m0 (host)"}.get(args.workload, scaled)
     if args.workload == "batched" and args.batch > 2:
         dtype = "fp4-e2m1 x bf16 -> fp32 accumulate"
     result.update(n_gpus=1, steps=K, warmup=W, higher_is_better=True, scaling="strong",
@@ -536,6 +708,10 @@ def main():
     ap.add_argument("--heads", default="40,10,128",
                     help="query heads, kv heads, head dim for --workload attention "
                          "(default Phi-4; gpt-oss-20b: 64,8,64)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="default workload: skip the sub-records")
+    ap.add_argument("--read-loads", type=int, default=0, choices=[0, 1, 2, 4, 8],
+                    help="loads per lane of the read ceiling (0: the fastest, swept)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",

@@ -63,6 +63,7 @@ _SIGS = {
     "tt_mxfp4_gateup_dequantize": (_I32, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
     "tt_int4_dequantize": (_I32, [_P, _I64, _I64, _I64, _P, _P]),
     "tt_fp8_dequantize": (_I32, [_P, _I64, _I64, _P, _P, _P]),
+    "tt_stream_read": (_I32, [_P, _I64, _I32, _P, _P]),
 }
 
 # libtt.so needs libamdhip64.so.7.  torch bundles its own HIP runtime under that
@@ -240,13 +241,37 @@ def _acts(x, name="x"):
     return x
 
 
+# The library cannot see buffer sizes (it takes raw pointers), so every size
+# is checked here before a call: a short buffer would otherwise become an
+# out-of-bounds device access.
+
+def _rows_of(x, k, name="x"):
+    """Tokens in x [batch][k]; x must hold a whole number of rows."""
+    if k <= 0 or x.numel() % k:
+        raise ValueError(f"{name} holds {x.numel()} elements, not a multiple of {k}")
+    return x.numel() // k
+
+
+def _holds(t, n, name):
+    if t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call needs {n}")
+
+
+def _packed(t, nbytes, name, count=1):
+    if t.numel() < nbytes * count:
+        what = f"{count} packs of {nbytes} bytes" if count > 1 else f"{nbytes} bytes"
+        raise ValueError(f"{name} holds {t.numel()} bytes, the call reads {what}")
+
+
 def mxfp4_gateup_swiglu(w_gu, inter, hidden, x, out=None, out_dtype=None):
     """SwiGLU(gate, up) of a packed gate/up pair for x [batch][hidden] bf16."""
     torch = _torch()
     _acts(x)
-    batch = x.numel() // hidden
+    batch = _rows_of(x, hidden)
+    _packed(w_gu, mxfp4_gateup_pack_bytes(inter, hidden), "w_gu")
     if out is None:
         out = torch.empty((batch, inter), dtype=out_dtype or torch.float32, device=x.device)
+    _holds(out, batch * inter, "out")
     _check(lib.tt_mxfp4_gateup_swiglu(_dev_ptr(w_gu, "w_gu", (torch.uint8,)), inter, hidden,
                                       _dev_ptr(x, "x"), batch, _dev_ptr(out, "out"),
                                       _dtype_code(out.dtype), _stream(x)))
@@ -261,6 +286,8 @@ def moe_route_topk(logits, topk, ids=None, w=None):
         ids = torch.empty((batch, topk), dtype=torch.int32, device=logits.device)
     if w is None:
         w = torch.empty((batch, topk), dtype=torch.float32, device=logits.device)
+    _holds(ids, batch * topk, "ids")
+    _holds(w, batch * topk, "w")
     _check(lib.tt_moe_route_topk(_dev_ptr(logits, "logits"), batch, n_exp, topk,
                                  _dev_ptr(ids, "ids", (torch.int32,)),
                                  _dev_ptr(w, "w", (torch.float32,)), _stream(logits)))
@@ -270,11 +297,14 @@ def moe_route_topk(logits, topk, ids=None, w=None):
 def moe_mxfp4_gateup_swiglu(bank, n_experts, inter, hidden, x, ids, out=None, out_dtype=None):
     torch = _torch()
     _acts(x)
-    batch = x.numel() // hidden
+    batch = _rows_of(x, hidden)
     topk = ids.shape[-1]
+    _holds(ids, batch * topk, "ids")
+    _packed(bank, mxfp4_gateup_pack_bytes(inter, hidden), "bank", n_experts)
     if out is None:
         out = torch.empty((batch, topk, inter), dtype=out_dtype or torch.float32,
                           device=x.device)
+    _holds(out, batch * topk * inter, "h")
     _check(lib.tt_moe_mxfp4_gateup_swiglu(_dev_ptr(bank, "bank", (torch.uint8,)), n_experts,
                                           inter, hidden, _dev_ptr(x, "x"), batch,
                                           _dev_ptr(ids, "ids", (torch.int32,)), topk,
@@ -289,7 +319,9 @@ def moe_mxfp4_route_gateup_swiglu(bank, n_experts, inter, hidden, x, logits, top
     torch = _torch()
     _acts(x)
     _acts(logits, "logits")
-    batch = x.numel() // hidden
+    batch = _rows_of(x, hidden)
+    _holds(logits, batch * n_experts, "logits")
+    _packed(bank, mxfp4_gateup_pack_bytes(inter, hidden), "bank", n_experts)
     if ids is None:
         ids = torch.empty((batch, topk), dtype=torch.int32, device=x.device)
     if w is None:
@@ -297,6 +329,9 @@ def moe_mxfp4_route_gateup_swiglu(bank, n_experts, inter, hidden, x, logits, top
     if out is None:
         out = torch.empty((batch, topk, inter), dtype=out_dtype or torch.float32,
                           device=x.device)
+    _holds(ids, batch * topk, "ids")
+    _holds(w, batch * topk, "w")
+    _holds(out, batch * topk * inter, "h")
     _check(lib.tt_moe_mxfp4_route_gateup_swiglu(
         _dev_ptr(bank, "bank", (torch.uint8,)), n_experts, inter, hidden, _dev_ptr(x, "x"), batch,
         _dev_ptr(logits, "logits"), topk, _dev_ptr(ids, "ids", (torch.int32,)),
@@ -309,8 +344,13 @@ def moe_mxfp4_down_combine(down_bank, n_experts, hidden, inter, h, ids, w, out=N
                            out_dtype=None):
     torch = _torch()
     batch, topk = ids.shape
+    if tuple(h.shape) != (batch, topk, inter):
+        raise ValueError(f"h has shape {tuple(h.shape)}, expected {(batch, topk, inter)}")
+    _holds(w, batch * topk, "w")
+    _packed(down_bank, mxfp4_matrix_pack_bytes(hidden, inter), "down_bank", n_experts)
     if out is None:
         out = torch.empty((batch, hidden), dtype=out_dtype or torch.float32, device=h.device)
+    _holds(out, batch * hidden, "y")
     _check(lib.tt_moe_mxfp4_down_combine(
         _dev_ptr(down_bank, "down_bank", (torch.uint8,)), n_experts, hidden, inter,
         _dev_ptr(h, "h", (torch.float32, torch.bfloat16)), _dtype_code(h.dtype),
@@ -322,9 +362,11 @@ def moe_mxfp4_down_combine(down_bank, n_experts, hidden, inter, h, ids, w, out=N
 def int4_gemv(w_packed, n, k, x, group=INT4_GROUP, out=None, out_dtype=None):
     torch = _torch()
     _acts(x)
-    batch = x.numel() // k
+    batch = _rows_of(x, k)
+    _packed(w_packed, int4_pack_bytes(n, k, group), "w_packed")
     if out is None:
         out = torch.empty((batch, n), dtype=out_dtype or torch.float32, device=x.device)
+    _holds(out, batch * n, "y")
     _check(lib.tt_int4_gemv(_dev_ptr(w_packed, "w_packed", (torch.uint8,)), n, k, group,
                             _dev_ptr(x, "x"), batch, _dev_ptr(out, "y"),
                             _dtype_code(out.dtype), _stream(x)))
@@ -336,9 +378,11 @@ def fp8_gemv(w_packed, n, k, x, out=None, out_dtype=None):
     bf16 (e.g. the gate/up SwiGLU output h)."""
     torch = _torch()
     _dev_ptr(x, "x", (torch.float32, torch.bfloat16))
-    batch = x.numel() // k
+    batch = _rows_of(x, k)
+    _packed(w_packed, fp8_pack_bytes(n, k), "w_packed")
     if out is None:
         out = torch.empty((batch, n), dtype=out_dtype or torch.float32, device=x.device)
+    _holds(out, batch * n, "y")
     _check(lib.tt_fp8_gemv(_dev_ptr(w_packed, "w_packed", (torch.uint8,)), n, k,
                            _dev_ptr(x, "x"), _dtype_code(x.dtype), batch, _dev_ptr(out, "y"),
                            _dtype_code(out.dtype), _stream(x)))
@@ -358,8 +402,12 @@ def gqa_attention_decode(q, k_cache, v_cache, hq, hkv, d, T, scale, out=None, ou
     for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _acts(t, name)
     tcap = k_cache.numel() // (hkv * d)
+    _holds(q, hq * d, "q")
+    if v_cache.numel() != k_cache.numel() or k_cache.numel() != hkv * tcap * d:
+        raise ValueError("k_cache and v_cache must both hold [hkv][tcap][d] elements")
     if out is None:
         out = torch.empty((hq, d), dtype=out_dtype or torch.float32, device=q.device)
+    _holds(out, hq * d, "out")
     need = gqa_attention_workspace_bytes(hq, hkv, d, T)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -372,6 +420,7 @@ def gqa_attention_decode(q, k_cache, v_cache, hq, hkv, d, T, scale, out=None, ou
 
 def mxfp4_dequantize(packed, n, k):
     torch = _torch()
+    _packed(packed, mxfp4_matrix_pack_bytes(n, k), "packed")
     w = torch.empty((n, k), dtype=torch.float32, device=packed.device)
     ps = torch.empty((n,), dtype=torch.float32, device=packed.device)
     _check(lib.tt_mxfp4_dequantize(_dev_ptr(packed, "packed", (torch.uint8,)), n, k,
@@ -381,6 +430,7 @@ def mxfp4_dequantize(packed, n, k):
 
 def mxfp4_gateup_dequantize(packed, inter, hidden):
     torch = _torch()
+    _packed(packed, mxfp4_gateup_pack_bytes(inter, hidden), "packed")
     mk = lambda *s: torch.empty(s, dtype=torch.float32, device=packed.device)  # noqa: E731
     g, u, gp, up = mk(inter, hidden), mk(inter, hidden), mk(inter), mk(inter)
     _check(lib.tt_mxfp4_gateup_dequantize(_dev_ptr(packed, "packed", (torch.uint8,)), inter,
@@ -392,6 +442,7 @@ def mxfp4_gateup_dequantize(packed, inter, hidden):
 
 def int4_dequantize(packed, n, k, group=INT4_GROUP):
     torch = _torch()
+    _packed(packed, int4_pack_bytes(n, k, group), "packed")
     w = torch.empty((n, k), dtype=torch.float32, device=packed.device)
     _check(lib.tt_int4_dequantize(_dev_ptr(packed, "packed", (torch.uint8,)), n, k, group,
                                   _dev_ptr(w, "w"), _stream(packed)))
@@ -400,11 +451,25 @@ def int4_dequantize(packed, n, k, group=INT4_GROUP):
 
 def fp8_dequantize(packed, n, k):
     torch = _torch()
+    _packed(packed, fp8_pack_bytes(n, k), "packed")
     w = torch.empty((n, k), dtype=torch.float32, device=packed.device)
     sc = torch.empty((n,), dtype=torch.float32, device=packed.device)
     _check(lib.tt_fp8_dequantize(_dev_ptr(packed, "packed", (torch.uint8,)), n, k,
                                  _dev_ptr(w, "w"), _dev_ptr(sc, "scale"), _stream(packed)))
     return w, sc
+
+
+def stream_read(buf, loads_per_lane=4, sink=None, nbytes=None):
+    """Measurement helper: read ``nbytes`` (default: all) of a uint8 device
+    tensor with 16-byte loads (the read ceiling of a streaming kernel)."""
+    torch = _torch()
+    n = buf.numel() if nbytes is None else int(nbytes)
+    _holds(buf, n, "buf")
+    if sink is None:
+        sink = torch.empty(1, dtype=torch.int32, device=buf.device)
+    _check(lib.tt_stream_read(_dev_ptr(buf, "buf", (torch.uint8,)), n, loads_per_lane,
+                              _dev_ptr(sink, "sink"), _stream(buf)))
+    return sink
 
 
 def normalize_device(dev):

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libtt.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["abi.cpp", "pack.cpp", "mxfp4_gateup.hip", "int4_gemv.hip", "moe.hip", "fp8_gemv.hip", "attention.hip",
-           "dequant.hip"]
+           "dequant.hip", "stream_read.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

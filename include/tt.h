@@ -5,9 +5,10 @@
  * What the calls compute follows the ThinTensor developer logs:
  *   - page kerbin.cskartikey.dev/@satvikhardat, "Dev Log #4 -- 91-96 tok/s
  *     with Selective MXFP4": MXFP4 on the MLP gate/up projections with a row
- *     postscale; the kernel reads packed FP4 weights and block scales,
- *     multiplies against BF16 activations, accumulates safely and then
- *     applies the row postscale (section "Where Blackwell helps");
+ *     postscale; out[r] = silu(ps_g[r] (Wg x)[r]) * (ps_u[r] (Wu x)[r]) over
+ *     4-bit codes with one power-of-two scale per 32 weights and bf16 x, the
+ *     postscale multiplying the finished row sum (section "Where Blackwell
+ *     helps");
  *   - same page, "Dev Log #2 -- Converting SafeTensors Into .thin": a dense
  *     MLP needs a gated activation; an MoE model has router and expert stages;
  *   - page stardance.hackclub.com/projects/29750, "numerical drift &
@@ -173,7 +174,10 @@ tt_status tt_quantize_int4_affine(const float *w, int64_t n, int64_t k,
 /* Bytes of a packed INT4 matrix. */
 int64_t tt_int4_pack_bytes(int64_t n, int64_t k, int64_t group);
 
-/* Pack a canonical INT4 matrix (q, s, z) into dst. */
+/* Pack a canonical INT4 matrix (q, s, z) into dst.  A group whose codes all
+ * equal its zero point (all of its weights are zero) is stored with a zero
+ * scale of the same sign: the decoded weights are the same bits, and the
+ * matvec then adds exactly 0 for that group. */
 tt_status tt_pack_int4(const uint8_t *q, const uint16_t *s, const uint16_t *z,
                        int64_t n, int64_t k, int64_t group,
                        void *dst, int64_t dst_bytes);
@@ -323,6 +327,7 @@ tt_status tt_gqa_attention_decode(const void *q, const void *k_cache, const void
                                   int64_t T, float scale, void *out, int32_t out_dtype,
                                   void *workspace, int64_t workspace_bytes, void *stream);
 
+
 /*
  * Decoded weights, for checking the packed layouts bit for bit: w[r][k] =
  * E2M1(code) * 2^(e-127) rounded once to fp32 (NaN for e = 0xFF).
@@ -343,6 +348,21 @@ tt_status tt_int4_dequantize(const void *packed, int64_t n, int64_t k,
  * [n] or NULL. */
 tt_status tt_fp8_dequantize(const void *packed, int64_t n, int64_t k,
                             float *w_out, float *scale_out, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* Measurement                                                             */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * A plain read of `bytes` bytes of device memory (16-byte aligned, a multiple
+ * of 16) with 16-byte loads: 256-lane workgroups, each lane issuing
+ * loads_per_lane (1, 2, 4 or 8) loads before using any.  Nothing of the
+ * method is computed; it is the bandwidth ceiling a streaming kernel of the
+ * same size can be compared with.  sink: 4 bytes of device memory, written
+ * only when the loaded data folds to one particular word.
+ */
+tt_status tt_stream_read(const void *buf, int64_t bytes, int32_t loads_per_lane,
+                         uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }
