@@ -59,6 +59,8 @@ _SIGS = {
     "tt_gqa_attention_workspace_bytes": (_I64, [_I64, _I64, _I64, _I64]),
     "tt_gqa_attention_decode": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64,
                                         ctypes.c_float, _P, _I32, _P, _I64, _P]),
+    "tt_gqa_attention_decode_noalloc": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64,
+                                                ctypes.c_float, _P, _I32, _P]),
     "tt_mxfp4_dequantize": (_I32, [_P, _I64, _I64, _P, _P, _P]),
     "tt_mxfp4_gateup_dequantize": (_I32, [_P, _I64, _I64, _P, _P, _P, _P, _P]),
     "tt_int4_dequantize": (_I32, [_P, _I64, _I64, _I64, _P, _P]),
@@ -415,6 +417,28 @@ def gqa_attention_decode(q, k_cache, v_cache, hq, hkv, d, T, scale, out=None, ou
         _dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"), hq, hkv,
         d, tcap, T, float(scale), _dev_ptr(out, "out"), _dtype_code(out.dtype),
         _dev_ptr(workspace, "workspace", (torch.uint8,)), workspace.numel(), _stream(q)))
+    return out
+
+
+def gqa_attention_decode_noalloc(q, k_cache, v_cache, hq, hkv, d, T, scale, out=None,
+                                 out_dtype=None):
+    """gqa_attention_decode with the partials in the library's own
+    per-device array instead of a workspace (the call allocates nothing on
+    the device; ``out`` is allocated here only when not given).  Calls that
+    overlap on one device share that array and must be ordered."""
+    torch = _torch()
+    for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _acts(t, name)
+    tcap = k_cache.numel() // (hkv * d)
+    _holds(q, hq * d, "q")
+    if v_cache.numel() != k_cache.numel() or k_cache.numel() != hkv * tcap * d:
+        raise ValueError("k_cache and v_cache must both hold [hkv][tcap][d] elements")
+    if out is None:
+        out = torch.empty((hq, d), dtype=out_dtype or torch.float32, device=q.device)
+    _holds(out, hq * d, "out")
+    _check(lib.tt_gqa_attention_decode_noalloc(
+        _dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"), hq, hkv,
+        d, tcap, T, float(scale), _dev_ptr(out, "out"), _dtype_code(out.dtype), _stream(q)))
     return out
 
 

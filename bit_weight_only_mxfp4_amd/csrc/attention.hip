@@ -17,6 +17,9 @@
 // A context of at most 256 / D chunks runs as one launch instead: one
 // workgroup per kv head, one wave per chunk, merged through LDS.  Chunks are
 // 64 positions, 32 for the split at contexts up to 2048.
+#include <atomic>
+#include <mutex>
+
 #include "device.h"
 #include "tt_internal.h"
 
@@ -453,11 +456,15 @@ extern "C" int64_t tt_gqa_attention_workspace_bytes(int64_t hq, int64_t hkv, int
     return hq * attn_chunks(d, T) * (d + 2) * 4;
 }
 
-extern "C" tt_status tt_gqa_attention_decode(const void *q, const void *k_cache,
-                                             const void *v_cache, int64_t hq, int64_t hkv,
-                                             int64_t d, int64_t tcap, int64_t T, float scale,
-                                             void *out, int32_t out_dtype, void *workspace,
-                                             int64_t workspace_bytes, void *stream) {
+namespace tt {
+namespace {
+
+// The checks and launches of one attention call, its per-chunk partials in
+// `workspace` (device memory of workspace_bytes).
+tt_status attn_decode(const void *q, const void *k_cache, const void *v_cache, int64_t hq,
+                      int64_t hkv, int64_t d, int64_t tcap, int64_t T, float scale, void *out,
+                      int32_t out_dtype, void *workspace, int64_t workspace_bytes,
+                      void *stream) {
     TT_TRY(check_ptr(q, "q"));
     TT_TRY(check_ptr(k_cache, "k_cache"));
     TT_TRY(check_ptr(v_cache, "v_cache"));
@@ -496,4 +503,70 @@ extern "C" tt_status tt_gqa_attention_decode(const void *q, const void *k_cache,
     tt_status st = d == 64 ? launch_attn_g<64>(a, (int)G, s) : launch_attn_g<128>(a, (int)G, s);
     if (st == TT_OK) clear_error();
     return st;
+}
+
+constexpr int64_t kAttnScratchBytes = TT_ATTN_SCRATCH_BYTES;
+
+}  // namespace
+
+// Partials of the allocation-free entry point: one array per device, held
+// until the process ends and shared by every such call on that device.  In
+// host code its name is only a stand-in; kernels get its device address,
+// looked up once per device.
+static __device__ __align__(256) uint8_t scratch[kAttnScratchBytes];
+
+namespace {
+
+std::atomic<void *> g_scratch_addr[64];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device (TT_E_HIP if the lookup
+// fails); looked up on the first call per device, with that device current.
+tt_status scratch_addr(void **ptr) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return fail(TT_E_HIP, "gqa attention (no allocation): no usable current device");
+    void *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p)
+                return fail(TT_E_HIP, "gqa attention (no allocation): scratch lookup failed: %s",
+                            hipGetErrorString(e));
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return TT_OK;
+}
+
+}  // namespace
+}  // namespace tt
+
+extern "C" tt_status tt_gqa_attention_decode(const void *q, const void *k_cache,
+                                             const void *v_cache, int64_t hq, int64_t hkv,
+                                             int64_t d, int64_t tcap, int64_t T, float scale,
+                                             void *out, int32_t out_dtype, void *workspace,
+                                             int64_t workspace_bytes, void *stream) {
+    return attn_decode(q, k_cache, v_cache, hq, hkv, d, tcap, T, scale, out, out_dtype,
+                       workspace, workspace_bytes, stream);
+}
+
+extern "C" tt_status tt_gqa_attention_decode_noalloc(const void *q, const void *k_cache,
+                                                     const void *v_cache, int64_t hq,
+                                                     int64_t hkv, int64_t d, int64_t tcap,
+                                                     int64_t T, float scale, void *out,
+                                                     int32_t out_dtype, void *stream) {
+    TT_TRY(check_attn_shape(hq, hkv, d, T));
+    const int64_t need = tt_gqa_attention_workspace_bytes(hq, hkv, d, T);
+    if (need > kAttnScratchBytes)
+        return fail(TT_E_SIZE, "gqa attention (no allocation): the call needs %lld bytes of "
+                    "partials, more than the %lld the library holds per device",
+                    (long long)need, (long long)kAttnScratchBytes);
+    void *ws = nullptr;
+    TT_TRY(scratch_addr(&ws));
+    return attn_decode(q, k_cache, v_cache, hq, hkv, d, tcap, T, scale, out, out_dtype, ws,
+                       kAttnScratchBytes, stream);
 }

@@ -326,6 +326,25 @@ tt_status tt_gqa_attention_decode(const void *q, const void *k_cache, const void
                                   int64_t hq, int64_t hkv, int64_t d, int64_t tcap,
                                   int64_t T, float scale, void *out, int32_t out_dtype,
                                   void *workspace, int64_t workspace_bytes, void *stream);
+/*
+ * tt_gqa_attention_decode without a workspace argument, for callers that
+ * cannot allocate device memory (code under stream capture that must not
+ * allocate, tight serving loops, harnesses that forbid allocation).  The
+ * per-chunk partials live in one array of TT_ATTN_SCRATCH_BYTES per device
+ * that the library holds from its first use on that device until the process
+ * ends; the call allocates nothing.  Same arguments, kernels and results as
+ * tt_gqa_attention_decode (the same bits).  TT_E_SIZE when
+ * tt_gqa_attention_workspace_bytes(hq, hkv, d, T) exceeds
+ * TT_ATTN_SCRATCH_BYTES (8 MiB: Phi-4-shaped heads 40 / 10 x 128 up to about
+ * 25,000 positions).  Every such call on one device shares that array, so
+ * calls that overlap on one device (two streams, or two host threads) race
+ * and must be ordered by the caller.
+ */
+#define TT_ATTN_SCRATCH_BYTES (8 << 20)
+tt_status tt_gqa_attention_decode_noalloc(const void *q, const void *k_cache,
+                                          const void *v_cache, int64_t hq, int64_t hkv,
+                                          int64_t d, int64_t tcap, int64_t T, float scale,
+                                          void *out, int32_t out_dtype, void *stream);
 
 
 /*
