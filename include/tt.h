@@ -194,10 +194,19 @@ tt_status tt_pack_int4(const uint8_t *q, const uint16_t *s, const uint16_t *z,
  *   out[b][r] = silu(g) * u,   silu(z) = z / (1 + e^-z)
  * w_gu: packed by tt_pack_mxfp4_gateup; x: bf16 [batch][hidden];
  * out: [batch][inter] of out_dtype (TT_F32 or TT_BF16, nearest-even).
- * 1 <= batch <= 32; hidden % 32 == 0, hidden <= TT_MAX_K.  Accumulation is
- * fp32.  Batch 1 and 2 run on the scaled FP4 x FP8 matrix instruction (each
- * bf16 activation carried exactly as two E4M3 parts); batch 3..32 on the
- * bf16 matrix cores.
+ * 1 <= batch <= 32; hidden % 32 == 0, hidden <= TT_MAX_K.
+ * Numerics.  Batch 1 and 2 run on the gfx950 scaled FP4 x FP8 matrix
+ * instruction: weights and E8M0 scales as stored, each bf16 activation
+ * carried exactly as two E4M3 parts (elements far below their block's
+ * largest lose bits below 2^(E-21)), every product exact; the instruction
+ * adds each 128-element block's products with a limited alignment width
+ * before its fp32 accumulator, so a block whose products span many binades
+ * is summed less exactly than in fp32.  Measured with products spread over
+ * up to 2^43 inside every block at K = 16384: at most 0.4 % of the
+ * 2e-3 * sum |w x| bound (random configs: about 0.1 %).  Batch 3..32 run on
+ * the bf16 matrix cores (weights times their block scale exact in bf16 for
+ * scale bytes 2..252, products exact, fp32 accumulation).  Partial sums are
+ * combined in a fixed order: the same bits on every run.
  */
 tt_status tt_mxfp4_gateup_swiglu(const void *w_gu, int64_t inter,
                                  int64_t hidden, const void *x, int64_t batch,
@@ -247,13 +256,18 @@ tt_status tt_moe_mxfp4_route_gateup_swiglu(const void *bank, int64_t n_experts,
                                            int32_t h_dtype, void *stream);
 
 /*
- * Routed-expert down projection and weighted combine:
+ * Routed-expert down projection and weighted combine ("Dev Log #2": an MoE
+ * model's expert stage after its router; "numerical drift & speedups":
+ * MXFP4 matvecs over the selected experts; the gpt-oss-20b-shaped layer
+ * runs gate/up SwiGLU and down per expert, weighted by the routing):
  *   y[b][r] = sum_{j = 0..topk-1, in order} w[b][j] * ps_d[e][r] *
  *             sum_k Wd[e][r][k] * h[b][j][k],      e = ids[b][j]
  * down_bank: n_experts packs of tt_mxfp4_matrix_pack_bytes(hidden, inter).
  * h: [batch][topk][inter] of h_dtype (TT_F32 or TT_BF16); w: f32
  * [batch][topk]; y: [batch][hidden] of y_dtype.  A bad id makes the whole
- * row NaN.  No atomics: the combine is one fixed-order sum per row.
+ * row NaN.  No atomics: the combine is one fixed-order sum per row.  bf16 h
+ * runs on the scaled FP4 x FP8 matrix instruction (the numerics of
+ * tt_mxfp4_gateup_swiglu at batch 1), fp32 h on the vector ALUs in fp32.
  */
 tt_status tt_moe_mxfp4_down_combine(const void *down_bank, int64_t n_experts,
                                     int64_t hidden, int64_t inter,
@@ -348,8 +362,11 @@ tt_status tt_gqa_attention_decode_noalloc(const void *q, const void *k_cache,
 
 
 /*
- * Decoded weights, for checking the packed layouts bit for bit: w[r][k] =
- * E2M1(code) * 2^(e-127) rounded once to fp32 (NaN for e = 0xFF).
+ * Decoded weights, for checking the packed layouts bit for bit (the formats
+ * the calls above read: MXFP4 of "Dev Log #4", with the OCP MX v1.0 element
+ * and scale encodings; affine INT4 of "Implemented a huge list of fixes";
+ * FP8 of "Dev Log #3"): w[r][k] = E2M1(code) * 2^(e-127) rounded once to
+ * fp32 (NaN for e = 0xFF).
  * tt_mxfp4_dequantize takes a tt_pack_mxfp4_matrix pack (w_out [n][k],
  * ps_out [n] or NULL); tt_mxfp4_gateup_dequantize takes a gate/up pack and
  * writes gate and up separately (any of the four outputs may be NULL, not
