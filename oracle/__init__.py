@@ -54,12 +54,19 @@ _libs = {}
 
 
 def lib(parallel: bool = False) -> ctypes.CDLL:
+    """The oracle library (the plain build, or the OpenMP timing build).
+    TT_ORACLE_LIB names another build of the same source to load instead of
+    the plain one (the sanitizer test runs the pins against an
+    AddressSanitizer / UBSan build this way)."""
     if parallel not in _libs:
-        if parallel:
-            _build_one(_LIB_OMP, ["-fopenmp"], False)
+        override = None if parallel else os.environ.get("TT_ORACLE_LIB")
+        if override:
+            path = override
+        elif parallel:
+            path = _build_one(_LIB_OMP, ["-fopenmp"], False)
         else:
-            build(force=False)
-        L = ctypes.CDLL(_LIB_OMP if parallel else _LIB)
+            path = build(force=False)
+        L = ctypes.CDLL(path)
         P, I64, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_double
         sig = {
             "or_e2m1_value": (D, [ctypes.c_int]),
