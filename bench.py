@@ -39,6 +39,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+# --graph-only: skip the eager timing (profiler runs, so that a kernel's
+# traced average covers graph-replayed dispatches only)
+GRAPH_ONLY = False
 
 
 def log(msg):
@@ -160,20 +163,22 @@ def rate(nbytes, seconds_per_call):
 
 # ---- read ceiling --------------------------------------------------------------
 
-def read_ceiling(tt, torch, bufs, nbytes, K, W, loads=4):
+def read_ceiling(tt, torch, bufs, nbytes, K, W, loads=4, calls=None):
     """A plain 16-byte-load read of nbytes from each of `bufs` in turn (the
-    same rotating buffers the kernel streams), captured as one graph like the
-    kernel's calls: seconds per read.  A buffer shorter than nbytes (a
-    weight pack without the call's activations and outputs) is read whole."""
+    same rotating buffers the kernel streams), `calls` reads per graph (one
+    per buffer by default) as the kernel's calls are captured: seconds per
+    read.  A buffer shorter than nbytes (a weight pack without the call's
+    activations and outputs) is read whole."""
     nbytes = min([nbytes] + [b.numel() for b in bufs])
     nbytes -= nbytes % 16
+    calls = calls or len(bufs)
     sink = torch.empty(1, dtype=torch.int32, device=bufs[0].device)
 
     def step():
-        for b in bufs:
-            tt.stream_read(b, loads, sink=sink, nbytes=nbytes)
+        for c in range(calls):
+            tt.stream_read(bufs[c % len(bufs)], loads, sink=sink, nbytes=nbytes)
 
-    return time_graph(torch, step, K, W) / (K * len(bufs)), nbytes
+    return time_graph(torch, step, K, W) / (K * calls), nbytes
 
 
 def best_read_loads(tt, torch, bufs, nbytes, K, W):
@@ -199,34 +204,45 @@ def vs_ceiling(rec, kernel_s, ceiling):
 
 # ---- workloads -------------------------------------------------------------------
 
-def measure_gateup(tt, torch, dev, w, batch, K, W, distinct=None, loads=4, ceiling=True):
+# decoder layers of the models the workloads are shaped like: one step (one
+# graph) holds one call per layer, cycling over the rotating weight copies
+MODEL_LAYERS = {"phi4": 40}
+
+
+def measure_gateup(tt, torch, dev, w, batch, K, W, distinct=None, loads=4, ceiling=True,
+                   calls=None):
     """Dense gate/up SwiGLU over `w.layers` rotating layers, one graph per
-    step.  loads = 0 sweeps the read ceiling's loads per lane on these
+    step of `calls` calls (default one per rotating layer) cycling over
+    them.  loads = 0 sweeps the read ceiling's loads per lane on these
     buffers and keeps the fastest.  Returns (record, per-call seconds)."""
     layers = w.layers
-    log(f"setup {w.name}: {layers} layers ({distinct or layers} generated), batch {batch}")
+    calls = calls or layers
+    log(f"setup {w.name}: {layers} layers ({distinct or layers} generated), batch {batch}, "
+        f"{calls} calls per step")
     packs, xs = setup_gateup(tt, torch, dev, w, layers, batch, distinct)
     outs = [torch.empty((batch, w.inter), dtype=torch.float32, device=dev)
             for _ in range(layers)]
 
     def step():
-        for i in range(layers):
+        for c in range(calls):
+            i = c % layers
             tt.mxfp4_gateup_swiglu(packs[i], w.inter, w.hidden, xs[i], out=outs[i])
 
-    eager = time_steps(torch, step, K, W) / (K * layers)
-    per_call = time_graph(torch, step, K, W) / (K * layers)
+    eager = None if GRAPH_ONLY else time_steps(torch, step, K, W) / (K * calls)
+    per_call = time_graph(torch, step, K, W) / (K * calls)
     nbytes = gateup_bytes(w.inter, w.hidden, batch)
     gbs, frac = rate(nbytes, per_call)
     rec = dict(workload=w.name, hidden=w.hidden, inter=w.inter, batch=batch,
-               us_per_call=round(per_call * 1e6, 3), us_per_call_eager=round(eager * 1e6, 3),
+               us_per_call=round(per_call * 1e6, 3),
+               us_per_call_eager=None if eager is None else round(eager * 1e6, 3),
                bytes_per_call=nbytes, gbs=gbs, frac_of_peak=frac,
                kernel="k_gateup_mx" if batch <= 2 else "k_gateup_mfma",
-               layers_rotated=layers)
+               layers_rotated=layers, calls_per_step=calls)
     if ceiling:
         if not loads:
             loads, rec["read_sweep_us"] = best_read_loads(tt, torch, packs, nbytes, K, W)
         rec["read_loads_per_lane"] = loads
-        vs_ceiling(rec, per_call, read_ceiling(tt, torch, packs, nbytes, K, W, loads))
+        vs_ceiling(rec, per_call, read_ceiling(tt, torch, packs, nbytes, K, W, loads, calls))
     return rec, per_call
 
 
@@ -325,22 +341,24 @@ def measure_int4(tt, torch, dev, K, W, loads=4):
             packs[name].append(packs[name][len(packs[name]) % distinct].clone())
     x = torch.from_numpy(workloads.activations(w.wid, 0, 1, kq, workloads.T_OX)
                          .view(np.int16)).to(dev)
+    calls = MODEL_LAYERS["phi4"]
     rec = {}
     for name, (n, k) in (("qkv", (nq, kq)), ("o", (no, ko))):
         y = torch.empty((1, n), dtype=torch.float32, device=dev)
         ps = packs[name]
 
         def step(ps=ps, n=n, k=k, y=y):
-            for p in ps:
-                tt.int4_gemv(p, n, k, x, out=y)
+            for c in range(calls):
+                tt.int4_gemv(ps[c % copies], n, k, x, out=y)
 
-        s = time_graph(torch, step, K, W) / (K * copies)
+        s = time_graph(torch, step, K, W) / (K * calls)
         nb = int4_bytes(n, k, 1)
         gbs, frac = rate(nb, s)
         rec[name] = vs_ceiling(dict(shape=[n, k], group=128, kernel="k_int4_gemv",
                                     us_per_call=round(s * 1e6, 3), bytes_per_call=nb, gbs=gbs,
-                                    frac_of_peak=frac),
-                               s, read_ceiling(tt, torch, ps, nb, K, W, loads))
+                                    frac_of_peak=frac, copies_rotated=copies,
+                                    calls_per_step=calls),
+                               s, read_ceiling(tt, torch, ps, nb, K, W, loads, calls))
     return rec
 
 
@@ -401,15 +419,16 @@ def run(args):
         # the read ceiling's loads per lane: swept on the headline's buffers
         # (the fastest plain read of its bytes), then used for every ceiling
         rec, per_call = measure_gateup(tt, torch, dev, w, batch, K, W, distinct,
-                                       args.read_loads, ceiling=args.workload != "tiny")
+                                       args.read_loads, ceiling=args.workload != "tiny",
+                                       calls=MODEL_LAYERS.get(args.workload))
         loads = rec.get("read_loads_per_lane", 4)
-        calls = K * w.layers
+        calls = K * rec["calls_per_step"]
         result = dict(metric=GATEUP_METRIC, value=rec["gbs"], unit="GB/s",
                       us_per_call=rec["us_per_call"], us_per_call_eager=rec["us_per_call_eager"],
-                      ms_per_step=round(per_call * w.layers * 1e3, 4),
+                      ms_per_step=round(per_call * rec["calls_per_step"] * 1e3, 4),
                       bytes_per_call=rec["bytes_per_call"],
                       config=dict(workload=w.name, hidden=w.hidden, inter=w.inter, batch=batch,
-                                  layers_rotated=w.layers, calls_per_step=w.layers,
+                                  layers_rotated=w.layers, calls_per_step=rec["calls_per_step"],
                                   launch="one HIP graph per step"),
                       roofline=dict(bound="hbm", kernel=rec["kernel"], achieved=rec["gbs"],
                                     peak=PEAK_HBM_GBS, unit="GB/s", frac=rec["frac_of_peak"],
@@ -427,7 +446,8 @@ def run(args):
             if not args.headline_only:
                 log("sub-records ...")
                 sub = {}
-                phi, _ = measure_gateup(tt, torch, dev, workloads.PHI4, 1, K, W, 4, loads)
+                phi, _ = measure_gateup(tt, torch, dev, workloads.PHI4, 1, K, W, 4, loads,
+                                        calls=MODEL_LAYERS["phi4"])
                 sub["phi4_gateup"] = phi
                 torch.cuda.empty_cache()
                 sub["gptoss_moe_layer"], _ = measure_moe(tt, torch, dev, K, W, loads)
@@ -447,9 +467,10 @@ def run(args):
         gbs, frac = rate(per_pair, secs)
         result = dict(metric="effective HBM GB/s of the grouped affine INT4 GEMV (QKV + O)",
                       value=gbs, unit="GB/s", us_per_call=round(secs / 2 * 1e6, 3),
-                      ms_per_step=round(secs * 16 * 1e3, 4),
+                      ms_per_step=round(secs * MODEL_LAYERS["phi4"] * 1e3, 4),
                       config=dict(workload="phi4-14b-int4-qkv-o", qkv=q["shape"], o=o["shape"],
                                   group=128, copies_rotated=16,
+                                  calls_per_step=MODEL_LAYERS["phi4"],
                                   launch="one HIP graph per projection and step"),
                       roofline=dict(bound="hbm", kernel="k_int4_gemv", achieved=gbs,
                                     peak=PEAK_HBM_GBS, unit="GB/s", frac=frac,
@@ -712,11 +733,15 @@ def main():
                     help="default workload: skip the sub-records")
     ap.add_argument("--read-loads", type=int, default=0, choices=[0, 1, 2, 4, 8],
                     help="loads per lane of the read ceiling (0: the fastest, swept)")
+    ap.add_argument("--graph-only", action="store_true",
+                    help="skip the eager timing (for profiler runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (profiler calibration)")
     args = ap.parse_args()
+    global GRAPH_ONLY
+    GRAPH_ONLY = args.graph_only
     if args.copy_probe:
         copy_probe(args.copy_probe, 4)
         return
