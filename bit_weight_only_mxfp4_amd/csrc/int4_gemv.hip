@@ -220,6 +220,27 @@ __global__ __launch_bounds__(1024) void k_int4_gemv(const uint8_t *w, const uint
     uint32_t bias;
     asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(bias));
     const uint32_t nib = 0x000F000Fu;
+    // the group sums of the wave's units for this lane's tokens, read before
+    // the first unit (16 bytes per four units) so that no unit waits on an
+    // LDS round trip of its own (measured: QKV 5.59 -> 5.44 us)
+    float xsv[4][UPW];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (e >= NT) break;
+        const int t = min(4 * q + e, NT - 1);
+#pragma unroll
+        for (int i4 = 0; i4 < UPW / 4; ++i4) {
+            const f32x4_t v = *reinterpret_cast<const f32x4_t *>(xsum + t * upk + u0 + 4 * i4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xsv[e][4 * i4 + j] = v[j];
+        }
+    }
+    // the activation operands of unit i + 1 are read from LDS while unit i
+    // runs on the matrix cores
+    const uint4 *xgb = reinterpret_cast<const uint4 *>(xs + ta * kp + (4 * u0 + q) * 32);
+    uint4 xcur[4], xnext[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) xcur[m] = xgb[m];
 #pragma unroll
     for (int i = 0; i < UPW; ++i) {
         const uint32_t sz = (i & 3) == 0 ? szv[i >> 2].x
@@ -227,7 +248,10 @@ __global__ __launch_bounds__(1024) void k_int4_gemv(const uint8_t *w, const uint
                           : (i & 3) == 2 ? szv[i >> 2].z : szv[i >> 2].w;
         const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(sz & 0xFFFFu));
         const float zb = 128.0f + (float)__builtin_bit_cast(_Float16, (uint16_t)(sz >> 16));
-        const uint4 *xg = reinterpret_cast<const uint4 *>(xs + ta * kp + (4 * (u0 + i) + q) * 32);
+        if (i + 1 < UPW) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) xnext[m] = xgb[(i + 1) * 16 + m];
+        }
         const uint32_t cw[4] = {c[i].x, c[i].y, c[i].z, c[i].w};
         f32x4_t cu = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -235,15 +259,19 @@ __global__ __launch_bounds__(1024) void k_int4_gemv(const uint8_t *w, const uint
             const uint4 wb = make_uint4(and_or(cw[m], nib, bias), and_or(cw[m] >> 4, nib, bias),
                                         and_or(cw[m] >> 8, nib, bias),
                                         and_or(cw[m] >> 12, nib, bias));
-            cu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xg[m]),
+            cu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xcur[m]),
                                                          __builtin_bit_cast(bf16x8_t, wb), cu, 0,
                                                          0, 0);
+        }
+        if (i + 1 < UPW) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) xcur[m] = xnext[m];
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int t = 4 * q + e;
             if (t < NT)
-                acc[e] = fmaf(s, fmaf(-zb, xsum[t * upk + u0 + i], cu[e]), acc[e]);
+                acc[e] = fmaf(s, fmaf(-zb, xsv[e][i], cu[e]), acc[e]);
         }
     }
     if (ks > 1) {
