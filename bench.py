@@ -324,11 +324,12 @@ def measure_moe(tt, torch, dev, K, W, loads=4):
 
 def measure_int4(tt, torch, dev, K, W, loads=4):
     """The Phi-4-shaped INT4 QKV (7680 x 5120) and O (5120 x 5120)
-    projections over 16 rotating copies, each projection timed alone."""
+    projections, one copy per Phi-4 layer (40, 1.4 GB: more than the 256 MB
+    last-level cache holds), each projection timed alone."""
     import workloads
     w = workloads.PHI4
     (nq, kq), (no, ko) = workloads.attention_shapes(w)
-    copies, distinct = 16, 2
+    copies, distinct = MODEL_LAYERS["phi4"], 2
     log(f"setup INT4 QKV [{nq}x{kq}] and O [{no}x{ko}], {copies} copies")
     packs = {"qkv": [], "o": []}
     for layer in range(distinct):

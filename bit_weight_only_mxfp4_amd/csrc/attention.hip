@@ -140,7 +140,7 @@ __global__ __launch_bounds__(64 * W) void k_attn_partial(const uint16_t *q, cons
         const int t = t0 + r;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             kr, (__attribute__((address_space(3))) void *)(s_k + u * 512), 16,
-            t < a.T ? (t * D + 8 * x) * 2 : kAttnOob, 0, 0, 0);
+            t < a.T ? (t * D + 8 * x) * 2 : kAttnOob, 0, 0, kStreamPolicy);
     }
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(64 * W) void k_attn_partial(const uint16_t *q, cons
         const int t = t0 + r;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             vr, (__attribute__((address_space(3))) void *)(s_v + u * 512), 16,
-            t < a.T ? (t * D + 8 * x) * 2 : kAttnOob, 0, 0, 0);
+            t < a.T ? (t * D + 8 * x) * 2 : kAttnOob, 0, 0, kStreamPolicy);
     }
 
     __builtin_amdgcn_sched_barrier(0);  // every DMA issued before the first read

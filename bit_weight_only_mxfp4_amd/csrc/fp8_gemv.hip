@@ -43,8 +43,10 @@ struct F8Args {
 
 constexpr int kF8Oob = 0x7FFFFF00;  // buffer offset past every range: loads return 0
 
+// 16-byte buffer load under cache policy POLICY (kStreamPolicy for weights)
+template <int POLICY>
 __device__ __forceinline__ uint4 f8_load16(__amdgpu_buffer_rsrc_t r, int off) {
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(1024) void k_fp8_gemv(const uint8_t *w, const void 
     for (int c = 0; c < XC; ++c) {
         const int t = c / XL, e0 = (cw0 + (c % XL) * 64 + lane) * EPC;
         const bool ok = t < nt && e0 < a.k;
-        xv[c] = f8_load16(xr, ok ? ((t0 + t) * a.k + e0) * (XF32 ? 4 : 2) : kF8Oob);
+        xv[c] = f8_load16<0>(xr, ok ? ((t0 + t) * a.k + e0) * (XF32 ? 4 : 2) : kF8Oob);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -128,10 +130,11 @@ __global__ __launch_bounds__(1024) void k_fp8_gemv(const uint8_t *w, const void 
     uint4 cu[UPW];
 #pragma unroll
     for (int i = 0; i < UPW; ++i)
-        cu[i] = f8_load16(rs, u0 + i < a.units ? (u0 + i) * kUnitBytes + lane * 16 : kF8Oob);
+        cu[i] = f8_load16<kStreamPolicy>(rs, u0 + i < a.units ? (u0 + i) * kUnitBytes + lane * 16 : kF8Oob);
     const float scale = __builtin_bit_cast(
         float, __builtin_amdgcn_raw_buffer_load_b32(
-                   rs, (wave == 0 && lane < kF8TileRows) ? a.scale_off + lane * 4 : kF8Oob, 0, 0));
+                   rs, (wave == 0 && lane < kF8TileRows) ? a.scale_off + lane * 4 : kF8Oob, 0,
+                   kStreamPolicy));
 
     // 3. the slice to LDS as it is (fp32 or bf16); only this wave reads it
     //    back, and a wave's LDS accesses complete in order: no barrier

@@ -217,17 +217,18 @@ __global__ __launch_bounds__(1024) void k_down_combine(const uint8_t *bank, cons
 #pragma unroll
         for (int g = 0; g < UPW / 4; ++g) {
             sd[g] = __builtin_amdgcn_raw_buffer_load_b32(
-                rs, 4 * g < n ? soff + g * kGroupBytes : kDownOob, 0, 0);
+                rs, 4 * g < n ? soff + g * kGroupBytes : kDownOob, 0, kStreamPolicy);
 #pragma unroll
             for (int i = 4 * g; i < 4 * g + 4; ++i) {
                 const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
-                    rs, i < n ? voff + i * kUnitBytes : kDownOob, 0, 0);
+                    rs, i < n ? voff + i * kUnitBytes : kDownOob, 0, kStreamPolicy);
                 c[i] = make_uint4(v.x, v.y, v.z, v.w);
             }
         }
         const float ps = __builtin_bit_cast(
             float, __builtin_amdgcn_raw_buffer_load_b32(
-                       rs, (part == 0 && lane < 16) ? a.ps_off + lane * 4 : kDownOob, 0, 0));
+                       rs, (part == 0 && lane < 16) ? a.ps_off + lane * 4 : kDownOob, 0,
+                       kStreamPolicy));
         const float wj = slot_ok ? a.wt[b * topk + j] : 0.0f;
 
         // 3. activations to the wave's own part of LDS (only this wave reads
@@ -330,17 +331,18 @@ __global__ __launch_bounds__(1024) void k_down_mx(const uint8_t *bank, const voi
 #pragma unroll
         for (int g = 0; g < UPW / 4; ++g) {
             sd[g] = __builtin_amdgcn_raw_buffer_load_b32(
-                rs, 4 * g < n ? soff + g * kGroupBytes : kDownOob, 0, 0);
+                rs, 4 * g < n ? soff + g * kGroupBytes : kDownOob, 0, kStreamPolicy);
 #pragma unroll
             for (int i = 4 * g; i < 4 * g + 4; ++i) {
                 const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
-                    rs, i < n ? voff + i * kUnitBytes : kDownOob, 0, 0);
+                    rs, i < n ? voff + i * kUnitBytes : kDownOob, 0, kStreamPolicy);
                 c[i] = make_uint4(v.x, v.y, v.z, v.w);
             }
         }
         const float ps = __builtin_bit_cast(
             float, __builtin_amdgcn_raw_buffer_load_b32(
-                       rs, (part == 0 && lane < 16) ? a.ps_off + lane * 4 : kDownOob, 0, 0));
+                       rs, (part == 0 && lane < 16) ? a.ps_off + lane * 4 : kDownOob, 0,
+                       kStreamPolicy));
         const float wj = slot_ok ? a.wt[b * topk + j] : 0.0f;
         __builtin_amdgcn_sched_barrier(0);
 

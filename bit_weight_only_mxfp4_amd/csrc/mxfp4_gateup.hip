@@ -171,7 +171,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, 
 }
 
 __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, int off) {
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStreamPolicy);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(1024) void k_gateup_mx(const uint8_t *w, const uint
 #pragma unroll
     for (int g = 0; g < UPW / 4; ++g) {
         sd[g] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * g < n ? soff + g * kGroupBytes : kOob,
-                                                     0, 0);
+                                                     0, kStreamPolicy);
 #pragma unroll
         for (int i = 4 * g; i < 4 * g + 4; ++i)
             c[i] = load16(rs, i < n ? voff + i * kUnitBytes : kOob);
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(1024) void k_gateup_mx(const uint8_t *w, const uint
     float ps_own = 0.0f;
     if (fin)  // uniform
         ps_own = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(rs, a.ps_off + (lane & 15) * 4, 0, 0));
+            float, __builtin_amdgcn_raw_buffer_load_b32(rs, a.ps_off + (lane & 15) * 4, 0, kStreamPolicy));
     // the routing outputs (their pointers come with the argument struct)
     if (a.logits && blockIdx.x == 0 && tid == 0) {
         a.ids_out[slot] = route_e;
@@ -477,7 +477,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_gateup_mfma(const uint8_t *
         const __amdgpu_buffer_rsrc_t rs =
             buffer_rsrc(a.w + (int64_t)(t0 + p) * a.tile_stride, a.tile_stride);
         ps4 = __builtin_bit_cast(
-            f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, a.ps_off + 16 * q, 0, 0));
+            f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, a.ps_off + 16 * q, 0, kStreamPolicy));
     }
 
     for (int kc = p; kc < nkc; kc += kMfmaWaves) {  // one round unless K > 2048
@@ -506,7 +506,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_gateup_mfma(const uint8_t *
             const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(
                 a.w + (int64_t)(ok ? t0 + t : 0) * a.tile_stride, ok ? a.tile_stride : 0);
             sd[t] = __builtin_amdgcn_raw_buffer_load_b32(
-                rs, a.scale_off + (u0 >> 2) * kGroupBytes + lane * 4, 0, 0);
+                rs, a.scale_off + (u0 >> 2) * kGroupBytes + lane * 4, 0, kStreamPolicy);
 #pragma unroll
             for (int u = 0; u < kMfmaUpc; ++u)
                 c[t][u] = load16(rs, u0 + u < a.units ? code_off(u0 + u, lane, a.units, a.qv_last)

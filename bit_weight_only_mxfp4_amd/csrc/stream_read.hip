@@ -1,5 +1,6 @@
 // stream_read.hip -- measurement helper: a plain read of a device buffer with
-// 16-byte loads, the ceiling the projection kernels are compared with.  It
+// 16-byte loads under the weight streams' cache policy (kStreamPolicy), the
+// ceiling the projection kernels are compared with.  It
 // does nothing of the method: every lane loads its 16-byte chunks, folds
 // them into one word and stores nothing unless that word has one particular
 // value (so the loads cannot be dropped and almost no store is made).
@@ -25,7 +26,7 @@ __global__ __launch_bounds__(kReadThreads) void k_stream_read(const uint8_t *buf
 #pragma unroll
     for (int u = 0; u < U; ++u)
         v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, (u * kReadThreads + threadIdx.x) * 16, 0,
-                                                     0);
+                                                     kStreamPolicy);
     uint32_t x = 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
