@@ -152,6 +152,13 @@ __global__ __launch_bounds__(64 * W) void k_attn_partial(const uint16_t *q, cons
     }
 
     __builtin_amdgcn_sched_barrier(0);  // every DMA issued before the first read
+    // the single workgroup writes the output after its last barrier
+    void *out = nullptr;
+    int32_t out_bf16 = 0;
+    if constexpr (W > 1) {
+        out = hold_sgpr(a.out);
+        out_bf16 = hold_sgpr(a.out_bf16);
+    }
     // key rows back as A operands: lane l takes row 16 b + l % 16 at d chunk
     // 4 kk + l / 16
     uint4 ka[NB][KK];
@@ -270,8 +277,8 @@ __global__ __launch_bounds__(64 * W) void k_attn_partial(const uint16_t *q, cons
 #pragma unroll
                 for (int w = 1; w < W; ++w) v = fmaf(s_o[w - 1][dt][lane][r], f[w], v);
                 if (head < G)
-                    store_out(a.out, (int64_t)(g * G + head) * D + dt * 16 + col, v / L,
-                              a.out_bf16);
+                    store_out(out, (int64_t)(g * G + head) * D + dt * 16 + col, v / L,
+                              out_bf16);
             }
         }
         return;

@@ -27,6 +27,17 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 // Phi-4 O projection ran 6 % slower and its QKV projection no faster.
 constexpr int kStreamPolicy = 2;
 
+// A kernel argument held in scalar registers from this point on.  Arguments
+// past the preloaded ones are otherwise read from argument memory where they
+// are used; after a workgroup barrier that read adds a memory round trip to
+// the end of the kernel.  Place it after the kernel's streaming loads are
+// issued, so the read overlaps them.
+template <typename T>
+__device__ __forceinline__ T hold_sgpr(T v) {
+    asm volatile("" : "+s"(v));
+    return v;
+}
+
 // E8M0 scale byte -> fp32 2^(e-127).  Byte 0 is the fp32 subnormal 2^-127,
 // byte 255 is NaN; every other byte is a normal power of two.
 __device__ __forceinline__ float e8m0_f32(uint32_t e) {

@@ -75,9 +75,12 @@ __device__ __forceinline__ uint2 f8x4_to_bf16x4(uint32_t c) {
 
 // The argument struct with the leading kernel parameters written in (they
 // are preloaded into scalar registers): everything read before the weight
-// loads; the tile geometry follows from k.
+// loads (the tile geometry follows from k), and the output, which the tail
+// after the last barrier needs (read from argument memory there, it would
+// add a memory round trip to the end of every call).
 __device__ __forceinline__ F8Args f8_hot_args(F8Args a, const uint8_t *w, const void *x,
-                                              int32_t k, int32_t batch, int32_t ks) {
+                                              int32_t k, int32_t batch, int32_t ks, int32_t n,
+                                              void *y, int32_t y_bf16) {
     const F8Geom g = f8_geom(k);
     a.w = w;
     a.x = x;
@@ -87,13 +90,17 @@ __device__ __forceinline__ F8Args f8_hot_args(F8Args a, const uint8_t *w, const 
     a.tile_stride = g.stride;
     a.batch = batch;
     a.ks = ks;
+    a.n = n;
+    a.y = y;
+    a.y_bf16 = y_bf16;
     return a;
 }
 
 template <int UPW, int NT, bool XF32>
 __global__ __launch_bounds__(1024) void k_fp8_gemv(const uint8_t *w, const void *x, int32_t k,
-                                                   int32_t batch, int32_t ks_, F8Args cold) {
-    const F8Args a = f8_hot_args(cold, w, x, k, batch, ks_);
+                                                   int32_t batch, int32_t ks_, int32_t rows,
+                                                   void *y, int32_t y_bf16, F8Args cold) {
+    const F8Args a = f8_hot_args(cold, w, x, k, batch, ks_, rows, y, y_bf16);
     extern __shared__ __align__(16) uint8_t smem[];
     const int ks = a.ks;
     constexpr int XSZ = XF32 ? 4 : 2;            // staged bytes per activation
@@ -243,7 +250,7 @@ tt_status launch_f8(F8Args a, hipStream_t s) {
     if (lds > 64 * 1024) TT_TRY((raise_lds_limit<k_fp8_gemv<UPW, NT, XF32>>("fp8 gemv")));
     dim3 grid((unsigned)a.ntiles, (unsigned)ceil_div(a.batch, NT));
     return launch("fp8 gemv", kern, grid, dim3(64 * a.ks), lds, s, a.w, a.x, a.k, a.batch, a.ks,
-                  a);
+                  a.n, a.y, a.y_bf16, a);
 }
 
 // registers a wave holds for loads in flight: its code units plus NT tokens'

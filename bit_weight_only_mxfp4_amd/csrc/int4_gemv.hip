@@ -71,9 +71,12 @@ __device__ __forceinline__ void i4_lds_barrier() {
 // activations and zero group sums, so they add exactly nothing.
 // The argument struct with the leading kernel parameters written in (they
 // are preloaded into scalar registers): everything read before the weight
-// loads; the tile geometry follows from k.
+// loads (the tile geometry follows from k), and the output, which the tail
+// after the last barrier needs (read from argument memory there, it would
+// add a memory round trip to the end of every call).
 __device__ __forceinline__ I4Args i4_hot_args(I4Args a, const uint8_t *w, const uint16_t *x,
-                                              int32_t k, int32_t batch, int32_t ks) {
+                                              int32_t k, int32_t batch, int32_t ks, int32_t n,
+                                              void *y, int32_t y_bf16) {
     const I4Geom g = i4_geom(k);
     a.w = w;
     a.x = x;
@@ -84,15 +87,19 @@ __device__ __forceinline__ I4Args i4_hot_args(I4Args a, const uint8_t *w, const 
     a.tile_stride = g.stride;
     a.batch = batch;
     a.ks = ks;
+    a.n = n;
+    a.y = y;
+    a.y_bf16 = y_bf16;
     return a;
 }
 
 template <int UPW, int NT, bool XVEC>
 __global__ __launch_bounds__(1024) void k_int4_gemv(const uint8_t *w, const uint16_t *x,
                                                     int32_t k, int32_t batch, int32_t ks_,
+                                                    int32_t rows, void *y, int32_t y_bf16,
                                                     I4Args cold) {
     static_assert(UPW % 4 == 0 && UPW <= 16, "units per wave");
-    const I4Args a = i4_hot_args(cold, w, x, k, batch, ks_);
+    const I4Args a = i4_hot_args(cold, w, x, k, batch, ks_, rows, y, y_bf16);
     extern __shared__ __align__(16) uint8_t smem[];
     const int ks = a.ks;
     const int kp = ks * UPW * 128;   // staged K per token, zero past a.k
@@ -314,9 +321,9 @@ tt_status launch_i4(I4Args a, hipStream_t s) {
     dim3 grid(a.ntiles, (a.batch + NT - 1) / NT);
     const size_t lds = lds_bytes(a.ks, UPW, NT);
     return a.xvec ? launch("int4 gemv", k_int4_gemv<UPW, NT, true>, grid, dim3(64 * a.ks), lds, s,
-                           a.w, a.x, a.k, a.batch, a.ks, a)
+                           a.w, a.x, a.k, a.batch, a.ks, a.n, a.y, a.y_bf16, a)
                   : launch("int4 gemv", k_int4_gemv<UPW, NT, false>, grid, dim3(64 * a.ks), lds, s,
-                           a.w, a.x, a.k, a.batch, a.ks, a);
+                           a.w, a.x, a.k, a.batch, a.ks, a.n, a.y, a.y_bf16, a);
 }
 
 template <int UPW>

@@ -107,11 +107,16 @@ struct DownArgs {
 // The argument struct with the leading kernel parameters of the down
 // kernels written in: everything read before the weight loads (the tile
 // geometry follows from the block count nb, K = inter = 32 nb; an expert's
-// pack is ceil(hidden / 16) whole tiles).
+// pack is ceil(hidden / 16) whole tiles), and the output, which the tail
+// after the last barrier needs (read from argument memory there, it would
+// add a memory round trip to the end of every call).  The first 14 dwords
+// of arguments are preloaded, so topk and the output's bf16 flag share one
+// (topk | bf16 << 16).
 __device__ __forceinline__ DownArgs down_hot_args(DownArgs a, const uint8_t *bank,
                                                   const void *h, const int32_t *ids, int32_t nb,
-                                                  int32_t n_experts, int32_t hidden, int32_t topk,
-                                                  int32_t S, int32_t spr) {
+                                                  int32_t n_experts, int32_t hidden,
+                                                  int32_t topk_yb, int32_t S, int32_t spr,
+                                                  void *y) {
     const MxGeom g = mx_geom(32 * (int64_t)nb);
     a.bank = bank;
     a.h = h;
@@ -126,9 +131,11 @@ __device__ __forceinline__ DownArgs down_hot_args(DownArgs a, const uint8_t *ban
     a.n_experts = n_experts;
     a.hidden = hidden;
     a.expert_stride = ceil_div(hidden, kTileRows) * g.stride;
-    a.topk = topk;
+    a.topk = topk_yb & 0xFFFF;
     a.S = S;
     a.spr = spr;
+    a.y = y;
+    a.y_bf16 = topk_yb >> 16;
     return a;
 }
 
@@ -153,6 +160,34 @@ __device__ __forceinline__ void down_lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// The combine after the down kernels' last barrier, run by all 64 lanes of
+// one wave: row r's output is the sum over slots j of w_j (ps_j[r] dot_j[r]),
+// dot_j = the slot's S partial rows summed in part order.  Lane (r = lane %
+// 16, quarter q = lane / 16) takes slots q and q + 4; it reads all parts of
+// a slot at once (indexes clamped into the table, the surplus masked off)
+// rather than one LDS round trip per part.  The quarters are then added as
+// (q0 + q1) + (q2 + q3) by lane swaps: a fixed order, the same bits on every
+// run.  A bad expert id's NaN weight makes the row NaN.
+static_assert(TT_MAX_TOPK <= 8, "two slots per quarter of the wave");
+__device__ __forceinline__ float down_combine_rows(const float *red, const float *pss, int topk,
+                                                   int S, int lane) {
+    const int r = lane & 15, q = lane >> 4;
+    float acc = 0.0f;
+#pragma unroll
+    for (int jq = 0; jq < 2; ++jq) {
+        const int jj = q + 4 * jq, jc = min(jj, topk - 1);
+        float v[16];  // S <= 16 parts
+#pragma unroll
+        for (int pp = 0; pp < 16; ++pp) v[pp] = red[(jc * S + min(pp, S - 1)) * 16 + r];
+        float dot = v[0];
+#pragma unroll
+        for (int pp = 1; pp < 16; ++pp) dot = pp < S ? dot + v[pp] : dot;
+        const float t = pss[jc * 17 + 16] * (pss[jc * 17 + r] * dot);
+        if (jj < topk) acc = jq == 0 ? t : acc + t;
+    }
+    return sum_xor32(sum_xor16(acc));
+}
+
 // fp32 h (vector ALUs; bf16 h takes the scaled-MFMA kernel below).  One
 // workgroup per (16-row output tile, token).  Slots are processed in rounds
 // of spr; within a round wave (slot j, part p) owns units
@@ -163,9 +198,10 @@ __device__ __forceinline__ void down_lds_barrier() {
 template <int UPW>
 __global__ __launch_bounds__(1024) void k_down_combine(const uint8_t *bank, const void *h,
                                                   const int32_t *ids, int32_t nb,
-                                                  int32_t n_experts, int32_t hidden, int32_t topk_,
-                                                  int32_t S_, int32_t spr_, DownArgs cold) {
-    const DownArgs a = down_hot_args(cold, bank, h, ids, nb, n_experts, hidden, topk_, S_, spr_);
+                                                  int32_t n_experts, int32_t hidden, int32_t topk_yb,
+                                                  int32_t S_, int32_t spr_, void *out,
+                                                  DownArgs cold) {
+    const DownArgs a = down_hot_args(cold, bank, h, ids, nb, n_experts, hidden, topk_yb, S_, spr_, out);
     static_assert(UPW % 4 == 0 && UPW <= 16, "units per wave");
     constexpr int ESZ = 4;                       // fp32 h
     constexpr int XC = UPW * ESZ / 8;            // 16-byte chunks per thread per round
@@ -254,17 +290,10 @@ __global__ __launch_bounds__(1024) void k_down_combine(const uint8_t *bank, cons
         }
     }
     down_lds_barrier();
-    if (wave != 0 || lane >= 16) return;
-    // fixed order: parts, then slots j = 0 .. topk - 1; a bad id (NaN weight)
-    // makes the row NaN
-    float y = 0.0f;
-    for (int jj = 0; jj < topk; ++jj) {
-        float dot = red[(jj * S) * 16 + lane];
-        for (int pp = 1; pp < S; ++pp) dot += red[(jj * S + pp) * 16 + lane];
-        y = fmaf(pss[jj * 17 + 16], pss[jj * 17 + lane] * dot, y);  // w_j (ps dot), one rounding
-    }
+    if (wave != 0) return;
+    const float y = down_combine_rows(red, pss, topk, S, lane);
     const int row = tile * 16 + lane;
-    if (row < a.hidden) store_out(a.y, (int64_t)b * a.hidden + row, y, a.y_bf16);
+    if (lane < 16 && row < a.hidden) store_out(a.y, (int64_t)b * a.hidden + row, y, a.y_bf16);
 }
 
 // Scaled-MFMA form of the same kernel for bf16 h: each unit goes to
@@ -277,9 +306,10 @@ __global__ __launch_bounds__(1024) void k_down_combine(const uint8_t *bank, cons
 template <int UPW>
 __global__ __launch_bounds__(1024) void k_down_mx(const uint8_t *bank, const void *h,
                                                   const int32_t *ids, int32_t nb,
-                                                  int32_t n_experts, int32_t hidden, int32_t topk_,
-                                                  int32_t S_, int32_t spr_, DownArgs cold) {
-    const DownArgs a = down_hot_args(cold, bank, h, ids, nb, n_experts, hidden, topk_, S_, spr_);
+                                                  int32_t n_experts, int32_t hidden, int32_t topk_yb,
+                                                  int32_t S_, int32_t spr_, void *out,
+                                                  DownArgs cold) {
+    const DownArgs a = down_hot_args(cold, bank, h, ids, nb, n_experts, hidden, topk_yb, S_, spr_, out);
     static_assert(UPW % 4 == 0 && UPW <= 16, "units per wave");
     constexpr int XC = UPW / 4;                  // 16-byte chunks per thread per round
     extern __shared__ __align__(16) uint8_t smem[];
@@ -397,15 +427,10 @@ __global__ __launch_bounds__(1024) void k_down_mx(const uint8_t *bank, const voi
         }
     }
     down_lds_barrier();
-    if (wave != 0 || lane >= 16) return;
-    float y = 0.0f;
-    for (int jj = 0; jj < topk; ++jj) {
-        float dot = red[(jj * S) * 16 + lane];
-        for (int pp = 1; pp < S; ++pp) dot += red[(jj * S + pp) * 16 + lane];
-        y = fmaf(pss[jj * 17 + 16], pss[jj * 17 + lane] * dot, y);  // w_j (ps dot), one rounding
-    }
+    if (wave != 0) return;
+    const float y = down_combine_rows(red, pss, topk, S, lane);
     const int row = tile * 16 + lane;
-    if (row < a.hidden) store_out(a.y, (int64_t)b * a.hidden + row, y, a.y_bf16);
+    if (lane < 16 && row < a.hidden) store_out(a.y, (int64_t)b * a.hidden + row, y, a.y_bf16);
 }
 
 }  // namespace tt
@@ -417,14 +442,14 @@ template <int UPW>
 tt_status launch_down_mx(const DownArgs &a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
     if (lds > 64 * 1024) TT_TRY((raise_lds_limit<k_down_mx<UPW>>("moe down + combine")));
     return launch("moe down + combine (scaled MFMA)", k_down_mx<UPW>, grid, block, lds, s, a.bank, a.h, a.ids, a.nb,
-                  a.n_experts, a.hidden, a.topk, a.S, a.spr, a);
+                  a.n_experts, a.hidden, a.topk | (a.y_bf16 << 16), a.S, a.spr, a.y, a);
 }
 
 template <int UPW>
 tt_status launch_down(const DownArgs &a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
     if (lds > 64 * 1024) TT_TRY((raise_lds_limit<k_down_combine<UPW>>("moe down + combine")));
     return launch("moe down + combine", k_down_combine<UPW>, grid, block, lds, s, a.bank, a.h, a.ids, a.nb,
-                  a.n_experts, a.hidden, a.topk, a.S, a.spr, a);
+                  a.n_experts, a.hidden, a.topk | (a.y_bf16 << 16), a.S, a.spr, a.y, a);
 }
 
 }  // namespace

@@ -260,12 +260,15 @@ tt_status tt_moe_mxfp4_route_gateup_swiglu(const void *bank, int64_t n_experts,
  * model's expert stage after its router; "numerical drift & speedups":
  * MXFP4 matvecs over the selected experts; the gpt-oss-20b-shaped layer
  * runs gate/up SwiGLU and down per expert, weighted by the routing):
- *   y[b][r] = sum_{j = 0..topk-1, in order} w[b][j] * ps_d[e][r] *
+ *   y[b][r] = sum_{j = 0..topk-1} w[b][j] * ps_d[e][r] *
  *             sum_k Wd[e][r][k] * h[b][j][k],      e = ids[b][j]
  * down_bank: n_experts packs of tt_mxfp4_matrix_pack_bytes(hidden, inter).
  * h: [batch][topk][inter] of h_dtype (TT_F32 or TT_BF16); w: f32
  * [batch][topk]; y: [batch][hidden] of y_dtype.  A bad id makes the whole
- * row NaN.  No atomics: the combine is one fixed-order sum per row.  bf16 h
+ * row NaN.  No atomics: each slot's K parts are summed in order, slot j's
+ * term is w_j (ps_d dot_j), and the terms are added in a fixed tree order
+ * (slots j and j + 4, then quarters (0 + 1) + (2 + 3)), the same bits on
+ * every run.  bf16 h
  * runs on the scaled FP4 x FP8 matrix instruction (the numerics of
  * tt_mxfp4_gateup_swiglu at batch 1), fp32 h on the vector ALUs in fp32.
  */
