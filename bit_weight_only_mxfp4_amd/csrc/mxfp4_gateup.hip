@@ -563,19 +563,55 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_gateup_mfma(const uint8_t *
     const int tile = t0 + p;
 #pragma unroll
     for (int cb = 0; cb < NCOL; ++cb) {
+        // the partial tiles of all K parts read at once (indexes clamped
+        // into the slices, the surplus masked off), summed in part order
         const f32x4_t *red = reinterpret_cast<const f32x4_t *>(smem) + (p * NCOL + cb) * 64 + lane;
         constexpr int kStride = mfma_slice_bytes<NCOL>() / 16;
-        f32x4_t y = red[0];
-        for (int s = 1; s < nparts; ++s) y += red[s * kStride];
+        f32x4_t v[kMfmaWaves];
+#pragma unroll
+        for (int s = 0; s < kMfmaWaves; ++s) v[s] = red[min(s, nparts - 1) * kStride];
+        f32x4_t y = v[0];
+#pragma unroll
+        for (int s = 1; s < kMfmaWaves; ++s)
+            if (s < nparts) y += v[s];
         // lane (token column r, row group q) holds rows 4q..4q+3 of the tile:
-        // gate rows in lanes 0..31, the matching up rows 32 lanes on
+        // gate rows in lanes 0..31, the matching up rows 32 lanes on (a
+        // half-wave swap brings them over)
+        float o[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float g = y[i] * ps4[i];
-            const float u = __shfl_down(g, 32);
-            const int token = cb * 16 + r, pair = tile * 8 + 4 * q + i;
-            if (lane < 32 && token < a.batch && pair < a.inter)
-                store_out(a.out, (int64_t)token * a.inter + pair, silu(g) * u, a.out_bf16);
+            const uint32_t gb = __builtin_bit_cast(uint32_t, g);
+            const f32x2_t sw =
+                __builtin_bit_cast(f32x2_t, __builtin_amdgcn_permlane32_swap(gb, gb, false, false));
+            o[i] = silu(g) * sw.y;
+        }
+        // pairs 4q .. 4q+3 of token cb*16 + r: one vector store when all four
+        // lie inside the row and the address is aligned
+        const int token = cb * 16 + r, pair0 = tile * 8 + 4 * q;
+        if (lane < 32 && token < a.batch) {
+            const int64_t at = (int64_t)token * a.inter + pair0;
+            if (a.out_bf16) {
+                uint16_t *dst = static_cast<uint16_t *>(a.out) + at;
+                if (pair0 + 3 < a.inter && (reinterpret_cast<uintptr_t>(dst) & 7) == 0) {
+                    *reinterpret_cast<uint2 *>(dst) =
+                        make_uint2(f32_to_bf16_bits(o[0]) | (uint32_t)f32_to_bf16_bits(o[1]) << 16,
+                                   f32_to_bf16_bits(o[2]) | (uint32_t)f32_to_bf16_bits(o[3]) << 16);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (pair0 + i < a.inter) dst[i] = f32_to_bf16_bits(o[i]);
+                }
+            } else {
+                float *dst = static_cast<float *>(a.out) + at;
+                if (pair0 + 3 < a.inter && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+                    *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (pair0 + i < a.inter) dst[i] = o[i];
+                }
+            }
         }
     }
 }

@@ -148,18 +148,43 @@ def test_batched_smollm3_every_row(dev, batch):
                                                 (96, 100, 3), (32, 8, 2), (5120, 24, 4),
                                                 (2048, 20000, 32), (2048, 11008, 23),
                                                 (256, 8192, 4), (1024, 16384, 20),
-                                                (256, 16384, 32), (512, 12000, 9)])
+                                                (256, 16384, 32), (512, 12000, 9),
+                                                (2880, 1001, 17), (96, 37, 5), (160, 1, 3),
+                                                (1024, 1002, 32)])
 def test_batched_ragged_shapes(dev, hidden, inter, batch):
     w = workloads.Workload(9, "ragged", hidden, inter)
     got, ref = _gateup_case(dev, w, 0, batch, guard=True)
     assert_parity(got, ref["h"], h_tol(ref), f"batched ragged h{hidden} i{inter} b{batch}")
 
 
-@pytest.mark.parametrize("batch", [1, 8])
-def test_bf16_output(dev, batch):
-    w = workloads.Workload(9, "bf16", 512, 300)
-    got, ref = _gateup_case(dev, w, 0, batch, out_dtype=torch.bfloat16)
+@pytest.mark.parametrize("batch,inter", [(1, 300), (8, 300), (8, 301), (32, 302)])
+def test_bf16_output(dev, batch, inter):
+    # odd and 2-mod-4 row lengths put rows off the 8-byte alignment of the
+    # batched kernel's 4-output stores (the element-wise fallback)
+    w = workloads.Workload(9, "bf16", 512, inter)
+    got, ref = _gateup_case(dev, w, 0, batch, out_dtype=torch.bfloat16, guard=True)
     assert_parity(got, ref["h"], h_tol(ref, bf16=True), f"bf16 out b{batch}")
+
+
+@pytest.mark.parametrize("batch,out_dtype", [(8, torch.float32), (32, torch.float32),
+                                             (8, torch.bfloat16)])
+def test_batched_output_off_alignment(dev, batch, out_dtype):
+    """An output that starts one element past an aligned address: the
+    batched kernel's 4-output stores must fall back to element stores."""
+    w = workloads.Workload(9, "offal", 1024, 400)
+    g, u = workloads.gateup(w)
+    x = workloads.activations(w.wid, 0, batch, w.hidden)
+    packed = dev_u8(tt.pack_mxfp4_gateup(g, u, w.inter, w.hidden), dev)
+    buf = torch.full((batch * w.inter + 2,), 7.0, dtype=out_dtype, device=dev)
+    out = buf[1:1 + batch * w.inter].view(batch, w.inter)
+    tt.mxfp4_gateup_swiglu(packed, w.inter, w.hidden, dev_bf16(x, dev), out=out,
+                           out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ends = buf[[0, -1]].float().cpu().numpy()
+    assert np.all(ends == 7.0), "element before or after the output was overwritten"
+    ref = oracle.mxfp4_gateup_swiglu(g, u, w.inter, w.hidden, x)
+    assert_parity(to_np(out), ref["h"], h_tol(ref, bf16=out_dtype == torch.bfloat16),
+                  f"offset output b{batch}")
 
 
 @pytest.mark.parametrize("batch", [1, 2, 16, 32])
