@@ -206,7 +206,9 @@ tt_status tt_pack_int4(const uint8_t *q, const uint16_t *s, const uint16_t *z,
  * 2e-3 * sum |w x| bound (random configs: about 0.1 %).  Batch 3..32 run on
  * the bf16 matrix cores (weights times their block scale exact in bf16 for
  * scale bytes 2..252, products exact, fp32 accumulation).  Partial sums are
- * combined in a fixed order: the same bits on every run.
+ * combined in a fixed order: the same bits on every run.  silu is evaluated
+ * with the hardware exp2 and reciprocal (within a few units in the last
+ * place of fp32).
  */
 tt_status tt_mxfp4_gateup_swiglu(const void *w_gu, int64_t inter,
                                  int64_t hidden, const void *x, int64_t batch,
