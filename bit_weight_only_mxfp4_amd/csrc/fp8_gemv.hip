@@ -160,17 +160,56 @@ __global__ __launch_bounds__(1024) void k_fp8_gemv(const uint8_t *w, const void 
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = 0.0f;
     if constexpr (XF32) {
-#pragma unroll
-        for (int i = 0; i < UPW; ++i) {
+        if constexpr (NT == 1) {
+            // unit i + 1's activations are read from LDS while unit i is
+            // summed (one token: the registers for it are free)
+            float4 xcur[NT][4], xnext[NT][4];
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                const float4 *xg = reinterpret_cast<const float4 *>(xs + t * kp +
-                                                                    kF8UnitK * (u0 + i) + 16 * q);
-                float d0 = f8x4_dot(cu[i].x, xg[0], 0.0f);
-                float d1 = f8x4_dot(cu[i].y, xg[1], 0.0f);
-                d0 = f8x4_dot(cu[i].z, xg[2], d0);
-                d1 = f8x4_dot(cu[i].w, xg[3], d1);
-                acc[t] += d0 + d1;
+                const float4 *xg =
+                    reinterpret_cast<const float4 *>(xs + t * kp + kF8UnitK * u0 + 16 * q);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) xcur[t][j] = xg[j];
+            }
+#pragma unroll
+            for (int i = 0; i < UPW; ++i) {
+                if (i + 1 < UPW) {
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        const float4 *xg = reinterpret_cast<const float4 *>(
+                            xs + t * kp + kF8UnitK * (u0 + i + 1) + 16 * q);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) xnext[t][j] = xg[j];
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    float d0 = f8x4_dot(cu[i].x, xcur[t][0], 0.0f);
+                    float d1 = f8x4_dot(cu[i].y, xcur[t][1], 0.0f);
+                    d0 = f8x4_dot(cu[i].z, xcur[t][2], d0);
+                    d1 = f8x4_dot(cu[i].w, xcur[t][3], d1);
+                    acc[t] += d0 + d1;
+                }
+                if (i + 1 < UPW) {
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) xcur[t][j] = xnext[t][j];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < UPW; ++i) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const float4 *xg = reinterpret_cast<const float4 *>(xs + t * kp +
+                                                                        kF8UnitK * (u0 + i) + 16 * q);
+                    float d0 = f8x4_dot(cu[i].x, xg[0], 0.0f);
+                    float d1 = f8x4_dot(cu[i].y, xg[1], 0.0f);
+                    d0 = f8x4_dot(cu[i].z, xg[2], d0);
+                    d1 = f8x4_dot(cu[i].w, xg[3], d1);
+                    acc[t] += d0 + d1;
+                }
             }
         }
         // the 8 pieces of each row -> row partial in lanes r (0..7)

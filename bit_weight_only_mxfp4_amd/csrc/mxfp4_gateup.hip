@@ -417,11 +417,22 @@ __global__ __launch_bounds__(1024) void k_gateup_mx(const uint8_t *w, const uint
     const float psg = (lane & 8) ? ps_other : ps_own;
     const float psu = (lane & 8) ? ps_own : ps_other;
     if (ft >= ntok) return;
+    // the K parts' partial rows, four LDS reads in flight at a time
+    // (indexes clamped into the table, the surplus masked), summed in order
     float g = 0.0f, u = 0.0f;
-    for (int p = 0; p < ks; ++p) {
-        const float *rp = red + ((tsub * ks + p) * NTOK + ft) * 16;
-        g += rp[fr];
-        u += rp[fr + 8];
+    for (int p0 = 0; p0 < ks; p0 += 4) {
+        float gv[4], uv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float *rp = red + ((tsub * ks + min(p0 + j, ks - 1)) * NTOK + ft) * 16;
+            gv[j] = rp[fr];
+            uv[j] = rp[fr + 8];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            g = p0 + j < ks ? g + gv[j] : g;
+            u = p0 + j < ks ? u + uv[j] : u;
+        }
     }
     const int pair = tile * 8 + fr;
     const int orow = routed ? slot : tok0 + ft;
