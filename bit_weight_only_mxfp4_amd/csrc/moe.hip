@@ -197,7 +197,7 @@ __device__ __forceinline__ float down_combine_rows(const float *red, const float
 // zero-length buffer descriptor, so its loads read nothing and return zeros.
 template <int UPW>
 __global__ __launch_bounds__(1024) void k_down_combine(const uint8_t *bank, const void *h,
-                                                  const int32_t *ids, int32_t nb,
+                                                  const int32_t *__restrict__ ids, int32_t nb,
                                                   int32_t n_experts, int32_t hidden, int32_t topk_yb,
                                                   int32_t S_, int32_t spr_, void *out,
                                                   DownArgs cold) {
@@ -224,11 +224,10 @@ __global__ __launch_bounds__(1024) void k_down_combine(const uint8_t *bank, cons
     for (int jb = 0; jb < topk; jb += spr) {
         const int j = jb + js;
         const bool slot_ok = j < topk;
-        const int e = slot_ok ? a.ids[b * topk + j] : -1;
-        const bool valid = e >= 0 && e < a.n_experts;
-
         // 1. the activations this wave's units read: slot j, chunks
-        //    part * UPW * 32 + c * 64 + lane (4 fp32 each)
+        //    part * UPW * 32 + c * 64 + lane (4 fp32 each); issued before
+        //    the expert id, whose wait they then overlap (the id is a scalar
+        //    load, counted apart from these vector loads)
         const int cw0 = part * UPW * 32;
         uint4 hv[XC];
 #pragma unroll
@@ -237,6 +236,9 @@ __global__ __launch_bounds__(1024) void k_down_combine(const uint8_t *bank, cons
             hv[c] = (slot_ok && ci < valid_chunks) ? hsrc[j * valid_chunks + ci]
                                                   : make_uint4(0, 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        const int e = slot_ok ? ids[b * topk + j] : -1;
+        const bool valid = e >= 0 && e < a.n_experts;
 
         // 2. weights
         const uint8_t *tb = valid ? a.bank + (int64_t)e * a.expert_stride +
@@ -305,7 +307,7 @@ __global__ __launch_bounds__(1024) void k_down_combine(const uint8_t *bank, cons
 // postscales / weights of the combine.
 template <int UPW>
 __global__ __launch_bounds__(1024) void k_down_mx(const uint8_t *bank, const void *h,
-                                                  const int32_t *ids, int32_t nb,
+                                                  const int32_t *__restrict__ ids, int32_t nb,
                                                   int32_t n_experts, int32_t hidden, int32_t topk_yb,
                                                   int32_t S_, int32_t spr_, void *out,
                                                   DownArgs cold) {
@@ -332,11 +334,10 @@ __global__ __launch_bounds__(1024) void k_down_mx(const uint8_t *bank, const voi
     for (int jb = 0; jb < topk; jb += spr) {
         const int j = jb + js;
         const bool slot_ok = j < topk;
-        const int e = slot_ok ? a.ids[b * topk + j] : -1;
-        const bool valid = e >= 0 && e < a.n_experts;
-
         // 1. the activations this wave's units read: slot j, chunks
-        //    part * UPW * 16 + c * 64 + lane (8 bf16 each)
+        //    part * UPW * 16 + c * 64 + lane (8 bf16 each); issued before
+        //    the expert id, whose wait they then overlap (the id is a scalar
+        //    load, counted apart from these vector loads)
         const int cw0 = part * UPW * 16;
         uint4 hv[XC];
 #pragma unroll
@@ -345,6 +346,9 @@ __global__ __launch_bounds__(1024) void k_down_mx(const uint8_t *bank, const voi
             hv[c] = (slot_ok && ci < valid_chunks) ? hsrc[j * valid_chunks + ci]
                                                   : make_uint4(0, 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        const int e = slot_ok ? ids[b * topk + j] : -1;
+        const bool valid = e >= 0 && e < a.n_experts;
 
         // 2. weights
         const uint8_t *tb = valid ? a.bank + (int64_t)e * a.expert_stride +
