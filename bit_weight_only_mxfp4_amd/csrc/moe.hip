@@ -169,23 +169,30 @@ __device__ __forceinline__ void down_lds_barrier() {
 // (q0 + q1) + (q2 + q3) by lane swaps: a fixed order, the same bits on every
 // run.  A bad expert id's NaN weight makes the row NaN.
 static_assert(TT_MAX_TOPK <= 8, "two slots per quarter of the wave");
-__device__ __forceinline__ float down_combine_rows(const float *red, const float *pss, int topk,
-                                                   int S, int lane) {
+template <int SMAX>
+__device__ __forceinline__ float down_combine_rows_n(const float *red, const float *pss, int topk,
+                                                     int S, int lane) {
     const int r = lane & 15, q = lane >> 4;
     float acc = 0.0f;
 #pragma unroll
     for (int jq = 0; jq < 2; ++jq) {
+        if (4 * jq >= topk) break;  // uniform: slots 4.. only when topk > 4
         const int jj = q + 4 * jq, jc = min(jj, topk - 1);
-        float v[16];  // S <= 16 parts
+        float v[SMAX];  // S <= SMAX parts
 #pragma unroll
-        for (int pp = 0; pp < 16; ++pp) v[pp] = red[(jc * S + min(pp, S - 1)) * 16 + r];
+        for (int pp = 0; pp < SMAX; ++pp) v[pp] = red[(jc * S + min(pp, S - 1)) * 16 + r];
         float dot = v[0];
 #pragma unroll
-        for (int pp = 1; pp < 16; ++pp) dot = pp < S ? dot + v[pp] : dot;
+        for (int pp = 1; pp < SMAX; ++pp) dot = pp < S ? dot + v[pp] : dot;
         const float t = pss[jc * 17 + 16] * (pss[jc * 17 + r] * dot);
         if (jj < topk) acc = jq == 0 ? t : acc + t;
     }
     return sum_xor32(sum_xor16(acc));
+}
+__device__ __forceinline__ float down_combine_rows(const float *red, const float *pss, int topk,
+                                                   int S, int lane) {
+    return S <= 4 ? down_combine_rows_n<4>(red, pss, topk, S, lane)
+                  : down_combine_rows_n<16>(red, pss, topk, S, lane);
 }
 
 // fp32 h (vector ALUs; bf16 h takes the scaled-MFMA kernel below).  One
