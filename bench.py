@@ -119,9 +119,35 @@ def profiled_traffic(kernel_sources, summary):
     return int(fields["traffic_bytes_per_launch"])
 
 
+# Before every timed measurement the device reads a separate 256 MB buffer
+# for SETTLE_S seconds (untimed, and not a benchmark step).  After the
+# host-side setup the GPU sits idle at low clocks, and the first ~15 ms of
+# work after idle ran up to 8 % slower than the steady state (Phi-4 gate/up:
+# 17.3-17.4 against 16.1 us per call in the first of six back-to-back
+# timings; SmolLM3: 6.02 against 5.96 us).  --settle-ms 0 turns it off.
+SETTLE_S = 0.1
+_settle = {}
+
+
+def settle(torch):
+    if SETTLE_S <= 0:
+        return
+    import bit_weight_only_mxfp4_amd as tt
+    if "buf" not in _settle:
+        _settle["buf"] = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        _settle["sink"] = torch.empty(1, dtype=torch.int32, device="cuda")
+    t0 = time.time()
+    while time.time() - t0 < SETTLE_S:
+        for _ in range(8):
+            tt.stream_read(_settle["buf"], 8, sink=_settle["sink"])
+        torch.cuda.synchronize()
+
+
 def time_steps(torch, step, steps, warmup):
     """`steps` back-to-back steps between two events recorded on the current
-    stream (the stream every call and graph replay here is launched on)."""
+    stream (the stream every call and graph replay here is launched on),
+    after the device has left its idle clocks and `warmup` untimed steps."""
+    settle(torch)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -691,7 +717,8 @@ def run(args):
         dtype = "fp4-e2m1 x bf16 -> fp32 accumulate"
     result.update(n_gpus=1, steps=K, warmup=W, higher_is_better=True, scaling="strong",
                   vs_baseline=None, dtype=dtype,
-                  data="synthetic (seeded codes, scales, postscales, activations)")
+                  data="synthetic (seeded codes, scales, postscales, activations)",
+                  settle_ms_before_each_timing=args.settle_ms)
     if "cpu_baseline" not in result:
         result["cpu_baseline"] = None
     order = ["metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
@@ -736,13 +763,18 @@ def main():
                     help="loads per lane of the read ceiling (0: the fastest, swept)")
     ap.add_argument("--graph-only", action="store_true",
                     help="skip the eager timing (for profiler runs)")
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="plain reads of a separate 256 MB buffer before each timed "
+                         "measurement, so that it starts at the device's working clocks "
+                         "(0: off)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (profiler calibration)")
     args = ap.parse_args()
-    global GRAPH_ONLY
+    global GRAPH_ONLY, SETTLE_S
     GRAPH_ONLY = args.graph_only
+    SETTLE_S = args.settle_ms / 1e3
     if args.copy_probe:
         copy_probe(args.copy_probe, 4)
         return
