@@ -451,8 +451,30 @@ __global__ __launch_bounds__(1024) void k_gateup_mx(const uint8_t *w, const uint
 // the matrix cores.  No workgroup barrier precedes the first MFMA.  The 8
 // partial tiles are then summed through LDS in a fixed order after one
 // barrier; the wave that finishes tile t (t = p) prefetched its postscales.
+// With 32 tokens (one workgroup per CU) a wave keeps only mfma_ahead() + 1
+// tiles' weights in flight and issues the next tile's as it starts on one:
+// the requests of the whole chip then reach memory roughly in tile order, so
+// every wave's first tiles land early and its matrix work overlaps the
+// stream instead of trailing it.  With 16 tokens (two workgroups per CU) the
+// whole run is issued at once, which measured faster there.
 constexpr int kMfmaWaves = 8;  // waves per workgroup = K-chunk stride
 constexpr int kMfmaUpc = 2;    // units per K-chunk
+
+template <int NCOL, int TMAX> constexpr int mfma_ahead() { return NCOL == 2 ? 2 : TMAX; }
+
+// Tile t of a run, K-chunk at unit u0, fetched inside the tile loop (the
+// same loads as the loop that fetches the first tiles)
+__device__ __forceinline__ void fetch_mfma_tile(const GateUpArgs &a, int t0, int t, int nt, int u0,
+                                                int lane, uint4 (&c)[kMfmaUpc], uint32_t &sd) {
+    const bool ok = t < nt;
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_rsrc(a.w + (int64_t)(ok ? t0 + t : 0) * a.tile_stride, ok ? a.tile_stride : 0);
+    sd = __builtin_amdgcn_raw_buffer_load_b32(rs, a.scale_off + (u0 >> 2) * kGroupBytes + lane * 4,
+                                              0, kStreamPolicy);
+#pragma unroll
+    for (int u = 0; u < kMfmaUpc; ++u)
+        c[u] = load16(rs, u0 + u < a.units ? code_off(u0 + u, lane, a.units, a.qv_last) : kOob);
+}
 
 template <int NCOL> constexpr int mfma_slice_bytes() { return NCOL * 16 * 512; }
 
@@ -507,12 +529,13 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_gateup_mfma(const uint8_t *
                 xr, (__attribute__((address_space(3))) void *)(slice + i * 1024), 16,
                 (t < a.batch && k < a.hidden) ? (t * a.hidden + k) * 2 : kOob, 0, 0, 0);
         }
-        // 2. weights of every tile of the run: the units' scale dword, then
-        //    the two units; tiles past the run read zeros
+        // 2. weights of the first kAhead tiles of the run: the units' scale
+        //    dword, then the two units; tiles past the run read zeros
+        constexpr int kAhead = mfma_ahead<NCOL, TMAX>();
         uint4 c[TMAX][kMfmaUpc];
         uint32_t sd[TMAX];
 #pragma unroll
-        for (int t = 0; t < TMAX; ++t) {
+        for (int t = 0; t < kAhead; ++t) {
             const bool ok = t < nt;
             const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(
                 a.w + (int64_t)(ok ? t0 + t : 0) * a.tile_stride, ok ? a.tile_stride : 0);
@@ -539,9 +562,15 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void k_gateup_mfma(const uint8_t *
                     xb[u][j][cb] =
                         *reinterpret_cast<const uint4 *>(slice + t * 512 + ((pc + t) & 31) * 16);
                 }
-        // 4. tile by tile, each as soon as its loads land
+        // 4. tile by tile, each as soon as its loads land; tile t + kAhead is
+        //    fetched before tile t is worked on
 #pragma unroll
         for (int t = 0; t < TMAX; ++t) {
+            if constexpr (kAhead < TMAX) {
+                if (t + kAhead < TMAX)
+                    fetch_mfma_tile(a, t0, t + kAhead, nt, u0, lane, c[t + kAhead], sd[t + kAhead]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
             for (int u = 0; u < kMfmaUpc; ++u) {
                 const float sc = e8m0_f32((sd[t] >> (8 * ((u0 + u) & 3))) & 255u);
@@ -717,10 +746,16 @@ tt_status launch_mfma(const GateUpArgs &a, hipStream_t stream) {
         TT_TRY((raise_lds_limit<k_gateup_mfma<NCOL, TMAX>>("mxfp4 gate/up (MFMA path)")));
     // as many workgroups as fit the CUs at once (two with 16 tokens, one with
     // 32), never more than TMAX tiles per workgroup (the split in the kernel
-    // is balanced): shorter runs put more waves on each SIMD
+    // is balanced): shorter runs put more waves on each SIMD.  With one
+    // workgroup per CU the longest run sets the time, so the tiles go out in
+    // runs of that length over as few workgroups as it takes, since each
+    // workgroup pulls the activations of all tokens over the whole K through
+    // L2 (128 KB at 32 tokens, K = 2048): 1376 tiles in runs of 6 take 230
+    // workgroups instead of 256.
     const int64_t per_cu = std::min<int64_t>(2, (int64_t)(kMaxLds / lds));
-    const int64_t blocks = std::max<int64_t>(
-        std::min<int64_t>(a.ntiles, per_cu * device_cus()), ceil_div(a.ntiles, TMAX));
+    const int64_t slots = per_cu * device_cus();
+    int64_t blocks = std::max<int64_t>(std::min<int64_t>(a.ntiles, slots), ceil_div(a.ntiles, TMAX));
+    if (per_cu == 1) blocks = ceil_div(a.ntiles, std::min<int64_t>(TMAX, ceil_div(a.ntiles, slots)));
     return launch("mxfp4 gate/up (MFMA path)", k_gateup_mfma<NCOL, TMAX>, dim3((unsigned)blocks),
                   dim3(64 * kMfmaWaves), lds, stream, a.w, a.x, a.nb, a.ntiles, a.batch, blocks, a);
 }
