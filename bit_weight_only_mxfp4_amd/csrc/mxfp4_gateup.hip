@@ -451,12 +451,14 @@ __global__ __launch_bounds__(1024) void k_gateup_mx(const uint8_t *w, const uint
 // the matrix cores.  No workgroup barrier precedes the first MFMA.  The 8
 // partial tiles are then summed through LDS in a fixed order after one
 // barrier; the wave that finishes tile t (t = p) prefetched its postscales.
-// With 32 tokens (one workgroup per CU) a wave keeps only mfma_ahead() + 1
-// tiles' weights in flight and issues the next tile's as it starts on one:
-// the requests of the whole chip then reach memory roughly in tile order, so
-// every wave's first tiles land early and its matrix work overlaps the
-// stream instead of trailing it.  With 16 tokens (two workgroups per CU) the
-// whole run is issued at once, which measured faster there.
+// With 32 tokens a wave keeps only mfma_ahead() + 1 tiles' weights in
+// flight and issues the next tile's as it starts on one: the requests of the
+// whole chip then reach memory roughly in tile order, so every wave's first
+// tiles land early and its matrix work overlaps the stream instead of
+// trailing it.  With one block of 16 tokens the whole run is issued at once,
+// which measured faster there.  Up to 8 tokens the runs are of 3 tiles at
+// two workgroups per CU, from 9 to 32 tokens of 6 tiles at one per CU (fewer
+// workgroups pull fewer copies of the activations through L2).
 constexpr int kMfmaWaves = 8;  // waves per workgroup = K-chunk stride
 constexpr int kMfmaUpc = 2;    // units per K-chunk
 
@@ -732,27 +734,23 @@ tt_status launch_scaled(GateUpArgs a, int slots, hipStream_t stream, int dense_b
 
 constexpr size_t kMaxLds = 160 * 1024;
 
-// Tiles per workgroup run: the weights of the whole run are in flight in
-// registers at once, and a wave's partial tiles fit its activation slice.
-template <int NCOL> constexpr int mfma_tmax() { return NCOL == 1 ? 3 : 6; }
-
 size_t mfma_lds(int ncol) { return (size_t)kMfmaWaves * ncol * 16 * 512; }
 
-template <int NCOL>
-tt_status launch_mfma(const GateUpArgs &a, hipStream_t stream) {
-    constexpr int TMAX = mfma_tmax<NCOL>();
+// Runs of at most TMAX tiles per workgroup (a wave's partial tiles fit its
+// activation slice), at most per_cu_max workgroups per CU.
+template <int NCOL, int TMAX>
+tt_status launch_mfma(const GateUpArgs &a, int per_cu_max, hipStream_t stream) {
     const size_t lds = mfma_lds(NCOL);
     if (lds > 64 * 1024)
         TT_TRY((raise_lds_limit<k_gateup_mfma<NCOL, TMAX>>("mxfp4 gate/up (MFMA path)")));
-    // as many workgroups as fit the CUs at once (two with 16 tokens, one with
-    // 32), never more than TMAX tiles per workgroup (the split in the kernel
-    // is balanced): shorter runs put more waves on each SIMD.  With one
-    // workgroup per CU the longest run sets the time, so the tiles go out in
-    // runs of that length over as few workgroups as it takes, since each
-    // workgroup pulls the activations of all tokens over the whole K through
-    // L2 (128 KB at 32 tokens, K = 2048): 1376 tiles in runs of 6 take 230
-    // workgroups instead of 256.
-    const int64_t per_cu = std::min<int64_t>(2, (int64_t)(kMaxLds / lds));
+    // as many workgroups as fit the CUs at once, never more than TMAX tiles
+    // per workgroup (the split in the kernel is balanced): shorter runs put
+    // more waves on each SIMD.  With one workgroup per CU the longest run
+    // sets the time, so the tiles go out in runs of that length over as few
+    // workgroups as it takes, since each workgroup pulls the activations of
+    // all its tokens over the whole K through L2 (128 KB at 32 tokens, K =
+    // 2048): 1376 tiles in runs of 6 take 230 workgroups instead of 256.
+    const int64_t per_cu = std::min<int64_t>(per_cu_max, (int64_t)(kMaxLds / lds));
     const int64_t slots = per_cu * device_cus();
     int64_t blocks = std::max<int64_t>(std::min<int64_t>(a.ntiles, slots), ceil_div(a.ntiles, TMAX));
     if (per_cu == 1) blocks = ceil_div(a.ntiles, std::min<int64_t>(TMAX, ceil_div(a.ntiles, slots)));
@@ -822,10 +820,12 @@ extern "C" tt_status tt_mxfp4_gateup_swiglu(const void *w_gu, int64_t inter, int
         st = launch_scaled(a, 1, s);
     else if (batch <= TT_GATEUP_MX_MAXB)
         st = launch_scaled(a, 1, s, (int)batch);
-    else if (batch <= 16)
-        st = launch_mfma<1>(a, s);
+    else if (batch <= 8)  // three-tile runs, two workgroups per CU
+        st = launch_mfma<1, 3>(a, 2, s);
+    else if (batch <= 16)  // six-tile runs, one workgroup per CU
+        st = launch_mfma<1, 6>(a, 1, s);
     else
-        st = launch_mfma<2>(a, s);
+        st = launch_mfma<2, 6>(a, 1, s);
     if (st == TT_OK) clear_error();
     return st;
 }
