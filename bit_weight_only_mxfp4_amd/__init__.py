@@ -96,8 +96,16 @@ def _np_ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
-def _host(a, dtype):
-    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+def _host(a, dtype, need=None, name="array"):
+    """Contiguous host copy (or view) of ``a``; with ``need``, ``a`` must hold
+    at least that many elements (the library reads them through a raw
+    pointer and cannot check)."""
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a, dtype=dtype)
+    if need is not None and a.size < need:
+        raise ValueError(f"{name} holds {a.size} elements, the call reads {need}")
+    return a
 
 
 def abi_version() -> int:
@@ -133,8 +141,10 @@ def int4_pack_bytes(n: int, k: int, group: int = INT4_GROUP) -> int:
 def pack_mxfp4_matrix(codes, scales, ps, n, k, out=None):
     """Canonical MXFP4 (codes u8[n][k/2], scales u8[n][k/32], ps f32[n] or
     None) -> packed uint8 numpy array (or into ``out``)."""
-    c, s, p = _host(codes, np.uint8), _host(scales, np.uint8), _host(ps, np.float32)
     nbytes = mxfp4_matrix_pack_bytes(n, k)
+    c = _host(codes, np.uint8, n * (k // 2), "codes")
+    s = _host(scales, np.uint8, n * (k // 32), "scales")
+    p = _host(ps, np.float32, n, "ps")
     dst = np.empty(nbytes, np.uint8) if out is None else out
     _check(lib.tt_pack_mxfp4_matrix(_np_ptr(c), _np_ptr(s), _np_ptr(p), n, k, _np_ptr(dst),
                                     dst.nbytes))
@@ -143,9 +153,11 @@ def pack_mxfp4_matrix(codes, scales, ps, n, k, out=None):
 
 def pack_mxfp4_gateup(g, u, inter, hidden, out=None):
     """g and u are canonical (codes, scales, ps) triples of [inter][hidden]."""
-    gc, gs, gp = _host(g[0], np.uint8), _host(g[1], np.uint8), _host(g[2], np.float32)
-    uc, us, up = _host(u[0], np.uint8), _host(u[1], np.uint8), _host(u[2], np.float32)
     nbytes = mxfp4_gateup_pack_bytes(inter, hidden)
+    nc, ns = inter * (hidden // 2), inter * (hidden // 32)
+    gc, gs = _host(g[0], np.uint8, nc, "gate codes"), _host(g[1], np.uint8, ns, "gate scales")
+    uc, us = _host(u[0], np.uint8, nc, "up codes"), _host(u[1], np.uint8, ns, "up scales")
+    gp, up = _host(g[2], np.float32, inter, "gate ps"), _host(u[2], np.float32, inter, "up ps")
     dst = np.empty(nbytes, np.uint8) if out is None else out
     _check(lib.tt_pack_mxfp4_gateup(_np_ptr(gc), _np_ptr(gs), _np_ptr(gp), _np_ptr(uc),
                                     _np_ptr(us), _np_ptr(up), inter, hidden, _np_ptr(dst),
@@ -160,8 +172,8 @@ def fp8_pack_bytes(n: int, k: int) -> int:
 def pack_fp8_matrix(codes, scale, n, k, out=None):
     """Canonical FP8 E4M3 codes u8[n][k] and row scales f32[n] (or None) ->
     packed uint8 numpy array (or into ``out``)."""
-    c, sc = _host(codes, np.uint8), _host(scale, np.float32)
     nbytes = fp8_pack_bytes(n, k)
+    c, sc = _host(codes, np.uint8, n * k, "codes"), _host(scale, np.float32, n, "scale")
     dst = np.empty(nbytes, np.uint8) if out is None else out
     _check(lib.tt_pack_fp8_matrix(_np_ptr(c), _np_ptr(sc), n, k, _np_ptr(dst), dst.nbytes))
     return dst
@@ -195,8 +207,10 @@ def quantize_int4_affine(w, group: int = INT4_GROUP):
 
 
 def pack_int4(q, s, z, n, k, group: int = INT4_GROUP, out=None):
-    q, s, z = _host(q, np.uint8), _host(s, np.uint16), _host(z, np.uint16)
     nbytes = int4_pack_bytes(n, k, group)
+    G = -(-k // group)
+    q = _host(q, np.uint8, n * (k // 2), "q")
+    s, z = _host(s, np.uint16, n * G, "s"), _host(z, np.uint16, n * G, "z")
     dst = np.empty(nbytes, np.uint8) if out is None else out
     _check(lib.tt_pack_int4(_np_ptr(q), _np_ptr(s), _np_ptr(z), n, k, group, _np_ptr(dst),
                             dst.nbytes))
@@ -221,6 +235,14 @@ def _dev_ptr(t, name, dtypes=None):
     if dtypes is not None and t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _same_device(ref, **tensors):
+    """Every tensor of a call on ref's device (the call runs on ref's current
+    stream; a buffer on another device would be read or written from there)."""
+    for name, t in tensors.items():
+        if t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, the call runs on {ref.device}")
 
 
 def _dtype_code(dt):
@@ -274,6 +296,7 @@ def mxfp4_gateup_swiglu(w_gu, inter, hidden, x, out=None, out_dtype=None):
     if out is None:
         out = torch.empty((batch, inter), dtype=out_dtype or torch.float32, device=x.device)
     _holds(out, batch * inter, "out")
+    _same_device(x, w_gu=w_gu, out=out)
     _check(lib.tt_mxfp4_gateup_swiglu(_dev_ptr(w_gu, "w_gu", (torch.uint8,)), inter, hidden,
                                       _dev_ptr(x, "x"), batch, _dev_ptr(out, "out"),
                                       _dtype_code(out.dtype), _stream(x)))
@@ -290,6 +313,7 @@ def moe_route_topk(logits, topk, ids=None, w=None):
         w = torch.empty((batch, topk), dtype=torch.float32, device=logits.device)
     _holds(ids, batch * topk, "ids")
     _holds(w, batch * topk, "w")
+    _same_device(logits, ids=ids, w=w)
     _check(lib.tt_moe_route_topk(_dev_ptr(logits, "logits"), batch, n_exp, topk,
                                  _dev_ptr(ids, "ids", (torch.int32,)),
                                  _dev_ptr(w, "w", (torch.float32,)), _stream(logits)))
@@ -307,6 +331,7 @@ def moe_mxfp4_gateup_swiglu(bank, n_experts, inter, hidden, x, ids, out=None, ou
         out = torch.empty((batch, topk, inter), dtype=out_dtype or torch.float32,
                           device=x.device)
     _holds(out, batch * topk * inter, "h")
+    _same_device(x, bank=bank, ids=ids, h=out)
     _check(lib.tt_moe_mxfp4_gateup_swiglu(_dev_ptr(bank, "bank", (torch.uint8,)), n_experts,
                                           inter, hidden, _dev_ptr(x, "x"), batch,
                                           _dev_ptr(ids, "ids", (torch.int32,)), topk,
@@ -334,6 +359,7 @@ def moe_mxfp4_route_gateup_swiglu(bank, n_experts, inter, hidden, x, logits, top
     _holds(ids, batch * topk, "ids")
     _holds(w, batch * topk, "w")
     _holds(out, batch * topk * inter, "h")
+    _same_device(x, bank=bank, logits=logits, ids=ids, w=w, h=out)
     _check(lib.tt_moe_mxfp4_route_gateup_swiglu(
         _dev_ptr(bank, "bank", (torch.uint8,)), n_experts, inter, hidden, _dev_ptr(x, "x"), batch,
         _dev_ptr(logits, "logits"), topk, _dev_ptr(ids, "ids", (torch.int32,)),
@@ -353,6 +379,7 @@ def moe_mxfp4_down_combine(down_bank, n_experts, hidden, inter, h, ids, w, out=N
     if out is None:
         out = torch.empty((batch, hidden), dtype=out_dtype or torch.float32, device=h.device)
     _holds(out, batch * hidden, "y")
+    _same_device(h, down_bank=down_bank, ids=ids, w=w, y=out)
     _check(lib.tt_moe_mxfp4_down_combine(
         _dev_ptr(down_bank, "down_bank", (torch.uint8,)), n_experts, hidden, inter,
         _dev_ptr(h, "h", (torch.float32, torch.bfloat16)), _dtype_code(h.dtype),
@@ -369,6 +396,7 @@ def int4_gemv(w_packed, n, k, x, group=INT4_GROUP, out=None, out_dtype=None):
     if out is None:
         out = torch.empty((batch, n), dtype=out_dtype or torch.float32, device=x.device)
     _holds(out, batch * n, "y")
+    _same_device(x, w_packed=w_packed, y=out)
     _check(lib.tt_int4_gemv(_dev_ptr(w_packed, "w_packed", (torch.uint8,)), n, k, group,
                             _dev_ptr(x, "x"), batch, _dev_ptr(out, "y"),
                             _dtype_code(out.dtype), _stream(x)))
@@ -385,6 +413,7 @@ def fp8_gemv(w_packed, n, k, x, out=None, out_dtype=None):
     if out is None:
         out = torch.empty((batch, n), dtype=out_dtype or torch.float32, device=x.device)
     _holds(out, batch * n, "y")
+    _same_device(x, w_packed=w_packed, y=out)
     _check(lib.tt_fp8_gemv(_dev_ptr(w_packed, "w_packed", (torch.uint8,)), n, k,
                            _dev_ptr(x, "x"), _dtype_code(x.dtype), batch, _dev_ptr(out, "y"),
                            _dtype_code(out.dtype), _stream(x)))
@@ -413,6 +442,7 @@ def gqa_attention_decode(q, k_cache, v_cache, hq, hkv, d, T, scale, out=None, ou
     need = gqa_attention_workspace_bytes(hq, hkv, d, T)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _same_device(q, k_cache=k_cache, v_cache=v_cache, out=out, workspace=workspace)
     _check(lib.tt_gqa_attention_decode(
         _dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"), hq, hkv,
         d, tcap, T, float(scale), _dev_ptr(out, "out"), _dtype_code(out.dtype),
@@ -436,6 +466,7 @@ def gqa_attention_decode_noalloc(q, k_cache, v_cache, hq, hkv, d, T, scale, out=
     if out is None:
         out = torch.empty((hq, d), dtype=out_dtype or torch.float32, device=q.device)
     _holds(out, hq * d, "out")
+    _same_device(q, k_cache=k_cache, v_cache=v_cache, out=out)
     _check(lib.tt_gqa_attention_decode_noalloc(
         _dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"), hq, hkv,
         d, tcap, T, float(scale), _dev_ptr(out, "out"), _dtype_code(out.dtype), _stream(q)))
@@ -491,6 +522,7 @@ def stream_read(buf, loads_per_lane=4, sink=None, nbytes=None):
     _holds(buf, n, "buf")
     if sink is None:
         sink = torch.empty(1, dtype=torch.int32, device=buf.device)
+    _same_device(buf, sink=sink)
     _check(lib.tt_stream_read(_dev_ptr(buf, "buf", (torch.uint8,)), n, loads_per_lane,
                               _dev_ptr(sink, "sink"), _stream(buf)))
     return sink

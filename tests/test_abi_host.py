@@ -83,6 +83,36 @@ def test_pack_sizes_and_size_errors():
     assert e.value.status == -5
 
 
+def test_packers_refuse_short_host_arrays():
+    """The packers read their inputs through raw pointers; a short array is
+    refused before the call instead of being read past its end."""
+    g, u = workloads.gateup(workloads.TINY)
+    with pytest.raises(ValueError, match="gate codes"):
+        tt.pack_mxfp4_gateup((g[0][:-1], g[1], g[2]), u, 512, 256)
+    with pytest.raises(ValueError, match="up ps"):
+        tt.pack_mxfp4_gateup(g, (u[0], u[1], u[2][:-1]), 512, 256)
+    codes, scales, ps = g
+    with pytest.raises(ValueError, match="scales"):
+        tt.pack_mxfp4_matrix(codes, scales[:-1], ps, 512, 256)
+    fc = np.zeros((8, 64), np.uint8)
+    with pytest.raises(ValueError, match="scale"):
+        tt.pack_fp8_matrix(fc, np.ones(7, np.float32), 8, 64)
+    q, sc, z = tt.quantize_int4_affine(np.ones((4, 256), np.float32))
+    with pytest.raises(ValueError, match="z"):
+        tt.pack_int4(q, sc, z[:-1], 4, 256)
+    # the full-size arrays still pack
+    tt.pack_int4(q, sc, z, 4, 256)
+    tt.pack_fp8_matrix(fc, np.ones(8, np.float32), 8, 64)
+
+
+def test_tensors_of_a_call_share_its_device():
+    torch = pytest.importorskip("torch")
+    a = torch.zeros(4)
+    tt._same_device(a, b=torch.zeros(2))
+    with pytest.raises(ValueError, match="b is on meta"):
+        tt._same_device(a, b=torch.zeros(2, device="meta"))
+
+
 def _unpack_mx(packed, nrows_tiles, k):
     """Read the documented tiled layout back into canonical arrays (tile row
     order): codes [16T][k/2], scales [16T][k/32], ps [16T]."""
