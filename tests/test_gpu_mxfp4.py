@@ -143,9 +143,10 @@ def test_batched_smollm3_every_row(dev, batch):
 # per tile, a single unit, tiles past the grid (each wave walks several
 # tiles), widths that fall back to one weight pass per token, workgroups
 # that own more tiles than a row has K-chunks (the finishing waves of the
-# later tiles never enter the K loop), and 32-token-path runs shorter than
+# later tiles never enter the K loop), 32-token-path runs shorter than
 # the longest allowed (2 and 5 tiles per workgroup, the second with 9
-# K-chunks, so two rounds of tile fetches).
+# K-chunks, so two rounds of tile fetches), and six-tile runs of one
+# 16-token block (2048 tiles: more workgroups than CUs; 9 K-chunks).
 @pytest.mark.parametrize("hidden,inter,batch", [(2880, 1000, 5), (4096, 520, 9), (2336, 1000, 32),
                                                 (96, 100, 3), (32, 8, 2), (5120, 24, 4),
                                                 (2048, 20000, 32), (2048, 11008, 23),
@@ -153,7 +154,8 @@ def test_batched_smollm3_every_row(dev, batch):
                                                 (256, 16384, 32), (512, 12000, 9),
                                                 (2880, 1001, 17), (96, 37, 5), (160, 1, 3),
                                                 (1024, 1002, 32), (512, 3000, 24),
-                                                (2304, 8200, 20)])
+                                                (2304, 8200, 20), (1024, 16384, 12),
+                                                (2304, 3000, 16)])
 def test_batched_ragged_shapes(dev, hidden, inter, batch):
     w = workloads.Workload(9, "ragged", hidden, inter)
     got, ref = _gateup_case(dev, w, 0, batch, guard=True)
