@@ -11,7 +11,7 @@
 //     (s * scale * log2(e), so each exponential is one v_exp_f32), positions
 //     past T read zeros and score -inf.  The chunk's (max, sum p, sum p V)
 //     per head go to the caller's workspace.
-//  2. k_attn_combine, one wave per (query head, 64 output columns): rescales
+//  2. k_attn_combine, one wave per (query head, 16 output columns): rescales
 //     the chunks to the global maximum and sums them in chunk order (fixed
 //     order: the result is the same on every run).
 // A context of at most 256 / D chunks runs as one launch instead: one
@@ -326,24 +326,28 @@ __device__ __forceinline__ float wave_reduce(float v) {
 __device__ __forceinline__ float wave_max(float v) { return wave_reduce<true>(v); }
 __device__ __forceinline__ float wave_sum(float v) { return wave_reduce<false>(v); }
 
-// One wave per (query head h = g * G + i, 64 output columns).  Rounds of 64
+// One wave per (query head h = g * G + i, 16 output columns).  Rounds of 64
 // chunks: lane k takes chunk c0 + k's (max, sum), and the wave maximum gives
-// every chunk's factor exp2(m_c - M); lane (phase c, column group q) takes
-// columns 4q .. 4q+3 of chunks 4u + c (16-byte loads: one instruction
-// covers four chunks x 64 columns, all issued before the first use), gets
-// each chunk's factor from the chunk's lane by ds_bpermute, and the four
-// phases are added in a fixed order (lane pairs 16 apart, then 32 apart).
-// Each round rescales the running sums to the new maximum.  No LDS and no
-// barrier.
+// every chunk's factor exp2(m_c - M); lane (phase c, column group q), lane =
+// 4c + q, takes columns 4q .. 4q+3 of chunks 16u + c (four 16-byte loads,
+// all issued before the first use), gets each chunk's factor from the
+// chunk's lane by ds_bpermute, and the 16 phases are added in a fixed order
+// (within each row of 16 lanes by rotates of 4 and 8 lanes, then across rows
+// by lane pairs 16 apart and 32 apart).  Each round rescales the running
+// sums to the new maximum.  No LDS and no barrier.  Narrow column slices
+// give four times the waves of 64-column ones, and each issues a quarter of
+// the loads.
+constexpr int kCombineCols = 16;
 template <int D, int G>
 __global__ __launch_bounds__(64) void k_attn_combine(const uint16_t *q, const uint16_t *k,
                                                      const uint16_t *v, float *part, float *ml,
                                                      int32_t tcap, int32_t T, int32_t nchunks,
                                                      float scale2, AttnArgs cold) {
+    constexpr int NG = kCombineCols / 4, PH = 64 / NG;  // column groups, chunk phases
     const AttnArgs a = attn_hot_args(cold, q, k, v, part, ml, tcap, T, nchunks, scale2);
     const int h = blockIdx.x, lane = threadIdx.x;
     const int g = h / G, i = h - g * G;
-    const int e0 = blockIdx.y * 64 + (lane & 15) * 4, ph = lane >> 4;
+    const int e0 = blockIdx.y * kCombineCols + (lane % NG) * 4, ph = lane / NG;
     const int nc = a.nchunks;
     const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
         a.part + (int64_t)g * nc * G * D, 0, nc * G * D * 4, 0x00020000);
@@ -355,10 +359,10 @@ __global__ __launch_bounds__(64) void k_attn_combine(const uint16_t *q, const ui
         const f32x2_t ml = __builtin_bit_cast(
             f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
                          mr, lane < n ? ((c0 + lane) * G + i) * 8 : kAttnOob, 0, 0));
-        f32x4_t pv[16];
+        f32x4_t pv[64 / PH];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int cu = 4 * u + ph;
+        for (int u = 0; u < 64 / PH; ++u) {
+            const int cu = PH * u + ph;
             pv[u] = __builtin_bit_cast(
                 f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                              pr, cu < n ? (((c0 + cu) * G + i) * D + e0) * 4 : kAttnOob, 0, 0));
@@ -371,14 +375,22 @@ __global__ __launch_bounds__(64) void k_attn_combine(const uint16_t *q, const ui
         L = fmaf(L, r, wave_sum(lane < n ? ml.y * f : 0.0f));
         float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
+        for (int u = 0; u < 64 / PH; ++u) {
             const float fu = __builtin_bit_cast(
-                float, __builtin_amdgcn_ds_bpermute((4 * u + ph) * 4, __builtin_bit_cast(int, f)));
+                float, __builtin_amdgcn_ds_bpermute((PH * u + ph) * 4, __builtin_bit_cast(int, f)));
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[j] = fmaf(pv[u][j], fu, acc[j]);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = fmaf(o[j], r, sum_xor32(sum_xor16(acc[j])));
+        for (int j = 0; j < 4; ++j) {
+            // the four phases of a row (lanes 4 apart), then the four rows
+            float t = acc[j];
+            t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                               0, __builtin_bit_cast(int, t), 0x124, 0xF, 0xF, false));
+            t += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                               0, __builtin_bit_cast(int, t), 0x128, 0xF, 0xF, false));
+            o[j] = fmaf(o[j], r, sum_xor32(sum_xor16(t)));
+        }
         M = Mn;
     }
     if (ph == 0)
@@ -424,7 +436,7 @@ tt_status launch_attn(const AttnArgs &a, hipStream_t s) {
         TT_TRY(launch_attn("gqa attention (chunks)", k_attn_partial<D, G, NB / 2, 1>,
                            dim3((unsigned)a.nchunks, (unsigned)a.hkv), dim3(64), s, a));
     return launch_attn("gqa attention (combine)", k_attn_combine<D, G>,
-                       dim3((unsigned)a.hq, (unsigned)(D / 64)), dim3(64), s, a);
+                       dim3((unsigned)a.hq, (unsigned)(D / kCombineCols)), dim3(64), s, a);
 }
 
 template <int D>
