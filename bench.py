@@ -16,8 +16,9 @@ with us_per_call, the roofline of the kernel, the read ceiling (a plain
 tt_stream_read) and the CPU oracle timed on the host (a reported baseline, not
 a target).  The default line also carries sub-records, each timed the same
 way against 8 TB/s and against its own read ceiling: the Phi-4-shaped gate/up,
-the gpt-oss-20b-shaped MoE layer (each kernel alone and the two together) and
-the Phi-4-shaped INT4 QKV and O projections (--headline-only skips them).
+the gpt-oss-20b-shaped MoE layer (each kernel alone and the two together), the
+Phi-4-shaped INT4 QKV and O projections and the batched gate/up at 8 and 32
+tokens (--headline-only skips them).
 
 Other workloads (--workload): tiny, phi4 (gate/up), phi4-int4 (QKV + O),
 gptoss (routing fused into the expert gate/up, then down/combine), batched
@@ -481,6 +482,12 @@ def run(args):
                 torch.cuda.empty_cache()
                 sub["phi4_int4"] = measure_int4(tt, torch, dev, K, W, loads)
                 torch.cuda.empty_cache()
+                # the batched config (SmolLM3 shapes) on the matrix-core path
+                sub["batched_gateup"] = {}
+                for b in (8, 32):
+                    sub["batched_gateup"][f"batch{b}"], _ = measure_gateup(
+                        tt, torch, dev, workloads.BATCHED, b, K, W, None, loads)
+                    torch.cuda.empty_cache()
                 result["subrecords"] = sub
         if not args.no_cpu_baseline and args.workload in ("smollm3", "tiny"):
             log("cpu baseline (oracle) ...")
